@@ -1,0 +1,212 @@
+"""Benchmark of one paged split-KV decode step on one MI355X.
+
+Workload (default): the 100K-token long-context decode -- batch 1, context
+100000, 32 query heads / 4 KV heads, head_dim 128, block_size 16, bf16 KV with
++8 logit outliers on 0.1% of keys, partition_size 512 (196 partitions).  One
+step is one full pass of the decode path over the batch: phase 1 (per-partition
+attention) + phase 2 (log-sum-exp merge), exactly what pa_decode enqueues for
+this shape, called through the C ABI.
+
+Inputs are resident in HBM before the timed region starts.  The KV pool is
+replicated R times and step i reads copy i mod R, so consecutive steps never
+find their KV in the 256 MB last-level cache: the figure is an HBM figure.
+
+Prints ONE JSON line.  Value = KV bytes read per step / step time (GB/s).
+The float64 oracle is used only in the CPU-baseline leg, which also checks the
+first step's GPU output against it.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = 100K context)")
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="KV pool replicas rotated across steps (0 = enough for >= 1 GiB)")
+    ap.add_argument("--variant", type=int, default=-1, help="matrix-core kernel variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def to_dev(a, dtype):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(w, seconds):
+    """Time the float64 oracle (as it stands) on the host cores over whole decode steps."""
+    import oracle
+    from paged_split_kv_pa_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ncores = len(os.sched_getaffinity(0))
+        ctx = threadpool_limits(limits=ncores)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy picks its own thread count
+        ctx, threads = None, len(os.sched_getaffinity(0))
+    kvb = wl.kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, w.dtype)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        ref = oracle.decode_attention(w.q, w.k_cache, w.v_cache, w.block_tables,
+                                      w.context_lens, w.scale, w.dtype)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 50:
+            break
+    if ctx is not None:
+        ctx.restore_original_limits()
+    return {"value": kvb * runs / el / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{runs} full decode steps of the same workload (float64 numpy oracle, "
+                      f"gather + upcast + softmax attention), {el:.1f} s wall"}, ref
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
+              "kernel is measured at one GPU's share of the work", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from paged_split_kv_pa_amd import binding as B
+    from paged_split_kv_pa_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.variant >= 0:
+        B.pa_set_mfma_variant(args.variant)
+
+    log(f"generating workload {wl.CONFIG_NAMES[args.config]}")
+    w = wl.config(args.config)
+    P = args.partition_size
+    kvb = wl.kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, w.dtype)
+    pool_bytes = w.k_cache.nbytes + w.v_cache.nbytes
+    R = args.copies if args.copies > 0 else max(2, -(-(1 << 30) // pool_bytes))
+    log(f"KV bytes/step {kvb}, pool {pool_bytes / 1e6:.1f} MB x {R} copies")
+
+    q = to_dev(w.q, w.dtype)
+    kc0, vc0 = to_dev(w.k_cache, w.dtype), to_dev(w.v_cache, w.dtype)
+    ks = [kc0] + [kc0.clone() for _ in range(R - 1)]
+    vs = [vc0] + [vc0.clone() for _ in range(R - 1)]
+    bt = torch.from_numpy(w.block_tables).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty(B.pa_workspace_bytes(q, kc0, bt, 0, P), dtype=torch.uint8, device="cuda")
+    path = B.pa_choose_path(B.dims_of(q, kc0, bt))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev0=None, ev1=None):
+        k, v = ks[i % R], vs[i % R]
+        if path == B.PA_PATH_V1:
+            if ev0 is not None:
+                ev0.record(stream)
+            B.pa_v1(out, q, k, v, bt, ctx, w.scale)
+            if ev1 is not None:
+                ev1.record(stream)
+            return
+        if ev0 is not None:
+            ev0.record(stream)
+        B.pa_v2_partition(out, q, k, v, bt, ctx, w.scale, ws, P)
+        if ev1 is not None:
+            ev1.record(stream)
+        B.pa_v2_reduce(out, q, k, bt, ctx, ws, P)
+
+    # First step: its output is kept and checked against the oracle in the CPU leg.
+    step(0)
+    torch.cuda.synchronize()
+    first_out = out.to(torch.float64).cpu().numpy()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev0[i], ev1[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]  # us, phase-1 launch
+    ms_per_step = wall * 1e3 / args.steps
+    k1_mean = float(np.mean(k1))
+    log(f"step {ms_per_step * 1e3:.2f} us; phase-1 kernel mean {k1_mean:.2f} us "
+        f"(median {np.median(k1):.2f}, p10 {np.percentile(k1, 10):.2f}, "
+        f"p90 {np.percentile(k1, 90):.2f})")
+
+    value = kvb / (ms_per_step / 1e3) / 1e9
+    achieved = kvb / (k1_mean / 1e6) / 1e9
+    rec = {
+        "metric": "KV-read GB/s (% of HBM peak) + us/decode step, paged attn at 100K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.CONFIG_NAMES[args.config],
+            "num_seqs": w.num_seqs, "context_lens_sum": int(w.context_lens.sum()),
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": wl.BLOCK_SIZE, "partition_size": P,
+            "path": "v1" if path == B.PA_PATH_V1 else "v2",
+            "kv_bytes_per_step": kvb, "kv_pool_copies": R,
+            "mfma_variant": B.pa_get_mfma_variant(),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "attn_mfma_kernel (phase 1)", "kernel_mean_us": round(k1_mean, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        rec["cpu_baseline"], ref = cpu_baseline(w, args.cpu_seconds)
+        err = np.abs(first_out - ref)
+        ok = bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
+        rel = float(np.max(np.linalg.norm((first_out - ref).reshape(-1, w.head_dim), axis=1) /
+                           np.linalg.norm(ref.reshape(-1, w.head_dim), axis=1)))
+        rec["parity"] = {"max_abs_err": float(err.max()), "max_row_rel_l2": rel,
+                         "within_tolerance": ok}
+        log(f"parity of the first timed-config step: max_abs_err={err.max():.3e} "
+            f"row_rel_l2={rel:.3e} ok={ok}")
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * pa_decode.h -- C ABI of the paged split-KV decode attention library for
+ * AMD Instinct MI355X (gfx950).  Library: libpa_decode.so.
+ *
+ * What the library computes.  One decode step of paged attention: for every
+ * sequence b and query head h, the softmax-weighted sum of the V rows of the
+ * context_lens[b] cached tokens, with weights softmax_t(scale * <q[b,h], K_t>).
+ * K_t / V_t are gathered through a block table from a paged KV cache.
+ * Sources (cited by page title and section):
+ *   - project_6 commit 96f4baf ("Dockerfile" commit page), V2 plan:
+ *     "Phase 1" per-(sequence, head, partition) attention storing a partial
+ *     output, an exp-sum and a max logit; "Phase 2" log-sum-exp merge; the
+ *     512-token partition size; V1 as a single pass over the whole context.
+ *   - project_6 optimizations/prefix_prefill_patch.py (commit fee8f1b),
+ *     "_PARTITION_SIZE inconsistency": both phases must use one partition size.
+ *     Here it is a single run-time argument, so they cannot disagree.
+ *   - project_6 commit a2a5dd8 ("computility-run.yaml" commit page), decode
+ *     path summary: V1 for contexts up to 8192 tokens, V2 above.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * All tensor pointers are DEVICE pointers, owned by the caller; the library
+ * never frees or retains them past the call.  Layouts are dense, row-major:
+ *   q, out          [S, Hq, D]          element type = dims->dtype
+ *   k_cache,v_cache [NB, Hkv, 16, D]    element type = dims->dtype
+ *   block_tables    [S, MB]   int32     physical block ids into the pool
+ *   context_lens    [S]       int32     tokens cached per sequence
+ * Token t of sequence b is slot (t % 16) of physical block
+ * block_tables[b][t / 16].  Query head h reads KV head h / (Hq / Hkv).
+ * Every tensor pointer must be 16-byte aligned (PA_ERR_ALIGN otherwise).
+ * out must not alias any input; it is fully overwritten (a sequence with no
+ * tokens gets 0).  out takes the element type of q, rounded to nearest even
+ * from the fp32 accumulator.
+ *
+ * Supported: dtype in {PA_F32, PA_F16, PA_BF16}; D in {128, 256};
+ * block_size == 16; G = Hq / Hkv in {1, 2, 4, 8, 16}.  partition_size must be
+ * a positive multiple of 16.
+ *
+ * Every call validates its arguments on the host before touching the GPU and
+ * returns a pa_status_t; pa_last_error() gives a message for the calling
+ * thread.  No host synchronisation happens: work is enqueued on `stream`
+ * (a hipStream_t; NULL means the default stream) and context_lens is only
+ * read on the device.  Block ids outside [0, NB) are read as block 0 and a
+ * context length above MB*16 is clamped to MB*16: such inputs give
+ * unspecified results but never an access outside the caller's buffers.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_DTYPE = -2,       /* unknown element type */
+  PA_ERR_SHAPE = -3,       /* inconsistent or non-positive sizes */
+  PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+  PA_ERR_PARTITION = -5,   /* partition_size <= 0 or not a multiple of block_size */
+  PA_ERR_UNSUPPORTED = -6, /* valid but not built: D, block_size, G, too many partitions */
+  PA_ERR_WORKSPACE = -7,   /* caller workspace NULL or smaller than pa_workspace_bytes() */
+  PA_ERR_HIP = -8,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_INTERNAL = -9
+} pa_status_t;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+/* Decode-path selector for pa_decode_ex. */
+enum { PA_PATH_AUTO = 0, PA_PATH_V1 = 1, PA_PATH_V2 = 2 };
+
+/* Problem sizes, passed by pointer to every entry point.  Plain integers. */
+typedef struct pa_dims {
+  int32_t num_seqs;           /* S   (0 is allowed: nothing to do) */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;           /* D */
+  int32_t block_size;         /* tokens per cache block; must be 16 */
+  int32_t num_blocks;         /* NB: blocks in the KV pool */
+  int32_t max_blocks_per_seq; /* MB: block_tables row length */
+  int32_t dtype;              /* pa_dtype_t of q, k_cache, v_cache and out */
+} pa_dims_t;
+
+/*
+ * pa_decode -- one decode step, path chosen by context length.
+ * The context bound used for planning is MB*16 (the block-table capacity); it
+ * picks V1 when it is <= the V1 threshold (pa_set_v1_max_context), else V2
+ * with partitions of partition_size tokens.  V2 uses a library-owned
+ * workspace that grows on demand (hipMalloc on the first call that needs
+ * more) and is kept per device; calls that overlap on one device from
+ * different streams must use pa_decode_ex with their own workspaces.
+ * Returns PA_OK or an error status; on error nothing was enqueued.
+ */
+pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, int32_t partition_size,
+                      void* stream);
+
+/*
+ * pa_workspace_bytes -- bytes of device workspace a V2 call needs.
+ * max_context_len <= 0 means MB*16.  Layout (all fp32, 256-byte aligned
+ * sections), with Pmax = ceil(max_context_len / partition_size):
+ *   tmp_out     [S, Hq, Pmax, D]  normalised partial output of each partition
+ *   max_logits  [S, Hq, Pmax]     max over the partition of scale*q.k
+ *   exp_sums    [S, Hq, Pmax]     sum over the partition of exp(logit - max)
+ * Returns 0 when the arguments are invalid (see pa_last_error()).
+ */
+size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
+                          int32_t partition_size);
+
+/*
+ * pa_decode_ex -- pa_decode with caller-chosen path, context bound and
+ * workspace.  path: PA_PATH_AUTO, PA_PATH_V1 or PA_PATH_V2.
+ * max_context_len: upper bound on every context_lens[b] (<= 0: MB*16); it
+ * sizes the partition grid, so a smaller bound means fewer idle work-groups.
+ * It must not exceed MB*16; tokens beyond it are not attended.
+ * workspace: device memory of >= pa_workspace_bytes(dims, max_context_len,
+ * partition_size) bytes, needed only when the path taken is V2 (may be NULL
+ * for V1).  Its contents after the call are the phase-1 partials (layout
+ * above) for sequences with more than one partition.
+ */
+pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, int32_t partition_size,
+                         void* stream, void* workspace, size_t workspace_bytes,
+                         int64_t max_context_len, int32_t path);
+
+/*
+ * pa_v2_partition -- V2 phase 1 alone (project_6 commit 96f4baf page,
+ * "Phase 1: Per-partition attention").  One work-group per (partition, KV
+ * head, sequence) computes, for every query head of the group, the partial
+ * output, exp-sum and max logit of its partition and writes them to the
+ * workspace (layout in pa_workspace_bytes).  A sequence whose context fits
+ * in one partition gets its final result written straight to out instead,
+ * and a sequence with no tokens gets out = 0.
+ */
+pa_status_t pa_v2_partition(const pa_dims_t* dims, void* out, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int32_t partition_size, int64_t max_context_len,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_v2_reduce -- V2 phase 2 alone (project_6 commit 96f4baf page, "Phase 2:
+ * Cross-partition reduction (log-sum-exp)").  For each (sequence, query
+ * head) with more than one partition: M = max_p max_logits[p],
+ * r_p = exp(max_logits[p] - M) * exp_sums[p], out = sum_p r_p tmp_out[p] /
+ * sum_p r_p.  Reads the workspace written by pa_v2_partition with the same
+ * dims, partition_size and max_context_len.
+ */
+pa_status_t pa_v2_reduce(const pa_dims_t* dims, void* out, const int32_t* context_lens,
+                         int32_t partition_size, int64_t max_context_len,
+                         const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_v1 -- V1: one pass over the whole context per (KV head, sequence), the
+ * single-launch path (project_6 commit 96f4baf page, V1 limitation note).
+ * Same arithmetic as phase 1 with one partition spanning max_context_len
+ * (<= 0: MB*16) tokens; writes out directly; needs no workspace.
+ */
+pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, float scale, int64_t max_context_len,
+                  void* stream);
+
+/* Path pa_decode would take for this context bound (<= 0: MB*16):
+ * PA_PATH_V1 or PA_PATH_V2, or a negative pa_status_t for invalid dims. */
+int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len);
+
+/* V1 threshold in tokens (V1 when the context bound is <= it).  Default 8192
+ * (project_6 commit a2a5dd8 page, decode path summary), or the value of the
+ * environment variable PA_V1_MAX_CONTEXT read at library load.  0 disables V1
+ * in the automatic choice.  Process-wide; safe to call from any thread. */
+void pa_set_v1_max_context(int64_t tokens);
+int64_t pa_get_v1_max_context(void);
+
+/* ceil(n / partition_size) for n >= 0 (0 for n == 0); -1 for invalid input. */
+int64_t pa_num_partitions(int64_t n, int32_t partition_size);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* pa_last_error(void);
+
+/* Frees the library-owned workspaces (all devices).  Must not overlap with
+ * a running pa_decode call. */
+void pa_release(void);
+
+/* Library version string, e.g. "pa_decode 0.1.0 gfx950". */
+const char* pa_version(void);
+
+/* Tuning knob for the fp16/bf16 kernel with G >= 4: work-group shape
+ *   0 = 2 waves per (partition, KV head, sequence), 3-deep (D=128) / 2-deep
+ *       (D=256) register pipeline per wave  [default]
+ *   1 = 1 wave, 5-deep / 3-deep pipeline
+ *   2 = 4 waves, 2-deep pipeline
+ * All variants compute the same result (to rounding).  The environment
+ * variable PA_MFMA_VARIANT sets the initial value.  Process-wide; do not
+ * change it while another thread is launching.  Returns PA_ERR_UNSUPPORTED
+ * for an unknown variant. */
+pa_status_t pa_set_mfma_variant(int32_t variant);
+int32_t pa_get_mfma_variant(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* PA_DECODE_H */

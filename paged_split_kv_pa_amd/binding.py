@@ -1,0 +1,272 @@
+"""Thin Python binding of libpa_decode.so (the C ABI in include/pa_decode.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+a ``pa_dims_t``; every step of the computation runs in the library's HIP
+kernels.  The functions keep the C names.  There is no fallback: if the
+library is missing or a call fails, a ``PaError`` is raised.
+
+Tensors (all on the same CUDA/HIP device, contiguous):
+  q, out           [S, Hq, D]        float32 / float16 / bfloat16
+  k_cache, v_cache [NB, Hkv, 16, D]  same dtype as q
+  block_tables     [S, MB]           int32
+  context_lens     [S]               int32
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libpa_decode.so")
+
+PA_OK = 0
+STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
+                -4: "PA_ERR_ALIGN", -5: "PA_ERR_PARTITION", -6: "PA_ERR_UNSUPPORTED",
+                -7: "PA_ERR_WORKSPACE", -8: "PA_ERR_HIP", -9: "PA_ERR_INTERNAL"}
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_PATH_AUTO, PA_PATH_V1, PA_PATH_V2 = 0, 1, 2
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+class PaDims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_DIMS = ctypes.POINTER(PaDims)
+
+# name -> (restype, argtypes); mirrors include/pa_decode.h
+SIGNATURES = {
+    "pa_decode": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P]),
+    "pa_workspace_bytes": (_SZ, [_DIMS, _I64, _I32]),
+    "pa_decode_ex": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _SZ,
+                            _I64, _I32]),
+    "pa_v2_partition": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _I64, _P,
+                               _SZ, _P]),
+    "pa_v2_reduce": (_I32, [_DIMS, _P, _P, _I32, _I64, _P, _SZ, _P]),
+    "pa_v1": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _P]),
+    "pa_choose_path": (_I32, [_DIMS, _I64]),
+    "pa_set_v1_max_context": (None, [_I64]),
+    "pa_get_v1_max_context": (_I64, []),
+    "pa_num_partitions": (_I64, [_I64, _I32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_release": (None, []),
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_set_mfma_variant": (_I32, [_I32]),
+    "pa_get_mfma_variant": (_I32, []),
+}
+
+_lib_handle = None
+
+
+def lib():
+    """Load libpa_decode.so once; raise if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise PaError(-9, f"HIP library not built: {LIB_PATH} is missing "
+                              "(run `python -m paged_split_kv_pa_amd.build`)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status):
+    if status != PA_OK:
+        raise PaError(status, pa_last_error())
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in codes:
+        raise PaError(-2, f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def dims_of(q, k_cache, block_tables):
+    """pa_dims_t from tensor shapes (q [S,Hq,D], k_cache [NB,Hkv,bs,D], table [S,MB])."""
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise PaError(-3, "q must be 3-D, k_cache 4-D and block_tables 2-D")
+    S, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D:
+        raise PaError(-3, f"head_dim of q ({D}) and k_cache ({Dk}) differ")
+    return PaDims(S, Hq, Hkv, D, bs, NB, block_tables.shape[1], _dtype_code(q))
+
+
+def _ptr(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise PaError(-1, f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise PaError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PaError(-3, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PaError(-2, f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tensors(out, q, k_cache, v_cache, block_tables, context_lens):
+    import torch
+    for name, t in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != q.dtype:
+            raise PaError(-2, f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise PaError(-3, "out must have the shape of q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise PaError(-3, "v_cache must have the shape of k_cache")
+    if context_lens.dim() != 1 or context_lens.shape[0] != q.shape[0] or \
+            block_tables.shape[0] != q.shape[0]:
+        raise PaError(-3, "block_tables and context_lens need one row per sequence")
+    return (_ptr(out, "out"), _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+            _ptr(block_tables, "block_tables", torch.int32),
+            _ptr(context_lens, "context_lens", torch.int32))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size=512,
+              stream=None):
+    """One decode step; path by context bound; library-owned workspace."""
+    d = dims_of(q, k_cache, block_tables)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    _check(lib().pa_decode(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
+                           _stream(stream)))
+    return out
+
+
+def pa_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=512):
+    d = dims_of(q, k_cache, block_tables)
+    n = lib().pa_workspace_bytes(ctypes.byref(d), int(max_context_len), int(partition_size))
+    if n == 0 and d.num_seqs > 0:
+        raise PaError(-3, pa_last_error())
+    return n
+
+
+def _ws(workspace):
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    return _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 partition_size=512, stream=None, workspace=None, max_context_len=0,
+                 path=PA_PATH_AUTO):
+    d = dims_of(q, k_cache, block_tables)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    _check(lib().pa_decode_ex(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
+                              _stream(stream), wp, wb, int(max_context_len), int(path)))
+    return out
+
+
+def pa_v2_partition(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+                    partition_size=512, max_context_len=0, stream=None):
+    d = dims_of(q, k_cache, block_tables)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    _check(lib().pa_v2_partition(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
+                                 int(max_context_len), wp, wb, _stream(stream)))
+    return out
+
+
+def pa_v2_reduce(out, q, k_cache, block_tables, context_lens, workspace, partition_size=512,
+                 max_context_len=0, stream=None):
+    import torch
+    d = dims_of(q, k_cache, block_tables)
+    wp, wb = _ws(workspace)
+    _check(lib().pa_v2_reduce(ctypes.byref(d), _ptr(out, "out"),
+                              _ptr(context_lens, "context_lens", torch.int32),
+                              int(partition_size), int(max_context_len), wp, wb,
+                              _stream(stream)))
+    return out
+
+
+def pa_v1(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len=0,
+          stream=None):
+    d = dims_of(q, k_cache, block_tables)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    _check(lib().pa_v1(ctypes.byref(d), *ptrs, float(scale), int(max_context_len),
+                       _stream(stream)))
+    return out
+
+
+def pa_choose_path(dims, max_context_len=0):
+    r = lib().pa_choose_path(ctypes.byref(dims), int(max_context_len))
+    if r < 0:
+        raise PaError(r, pa_last_error())
+    return r
+
+
+def pa_set_v1_max_context(tokens):
+    lib().pa_set_v1_max_context(int(tokens))
+
+
+def pa_get_v1_max_context():
+    return int(lib().pa_get_v1_max_context())
+
+
+def pa_num_partitions(n, partition_size):
+    return int(lib().pa_num_partitions(int(n), int(partition_size)))
+
+
+def pa_last_error():
+    msg = lib().pa_last_error()
+    return msg.decode() if msg else ""
+
+
+def pa_release():
+    lib().pa_release()
+
+
+def pa_version():
+    return lib().pa_version().decode()
+
+
+def pa_set_mfma_variant(variant):
+    _check(lib().pa_set_mfma_variant(int(variant)))
+
+
+def pa_get_mfma_variant():
+    return int(lib().pa_get_mfma_variant())
+
+
+def workspace_layout(q, k_cache, block_tables, max_context_len=0, partition_size=512):
+    """Views into a V2 workspace: offsets and shapes of tmp_out / max_logits / exp_sums.
+
+    Mirrors the layout documented for pa_workspace_bytes (fp32 sections, each
+    starting on a 256-byte boundary).
+    """
+    S, Hq, D = q.shape
+    cap = block_tables.shape[1] * k_cache.shape[2]
+    bound = max_context_len if max_context_len > 0 else cap
+    pmax = -(-bound // partition_size)
+    rows = S * Hq * pmax
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off_max = a256(rows * D * 4)
+    off_sum = off_max + a256(rows * 4)
+    return {"pmax": pmax, "tmp_out": (0, (S, Hq, pmax, D)),
+            "max_logits": (off_max, (S, Hq, pmax)), "exp_sums": (off_sum, (S, Hq, pmax)),
+            "bytes": off_sum + a256(rows * 4)}

@@ -1,0 +1,404 @@
+// C-ABI front end of libpa_decode.so: argument validation, planning (path,
+// partition grid, workspace layout) and kernel dispatch.  Declarations and
+// the contract of every entry point are in include/pa_decode.h.
+//
+// Validation is pure host arithmetic and runs before the first HIP call, so
+// every error status can be produced without a GPU.  The only host-side HIP
+// calls are hipGetDevice / hipMalloc / hipFree for the library-owned
+// workspace of pa_decode, hipGetLastError after launches, and the launches.
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <string>
+
+#include "pa_decode.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+std::atomic<int64_t>& v1_threshold() {
+  static std::atomic<int64_t> t([] {
+    const char* env = std::getenv("PA_V1_MAX_CONTEXT");
+    if (env && *env) {
+      char* end = nullptr;
+      long long v = std::strtoll(env, &end, 10);
+      if (end && *end == '\0' && v >= 0) return (int64_t)v;
+    }
+    return (int64_t)8192;  // V1 up to 8192 tokens: project_6 commit a2a5dd8 page, decode paths
+  }());
+  return t;
+}
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status_t ok() { return PA_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int element_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+// Sizes derived from validated dims.
+struct Plan {
+  int S, Hq, Hkv, D, G, NB, MB;
+  int64_t ctx_bound;  // planning bound on every context length
+  int32_t P;          // partition size used by the kernels
+  int64_t Pmax;       // partition-grid size
+  size_t off_tmp, off_max, off_sum, ws_bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+pa_status_t check_dims(const pa_dims_t* d) {
+  if (!d) return fail(PA_ERR_NULL, "dims is NULL");
+  if (d->dtype != PA_F32 && d->dtype != PA_F16 && d->dtype != PA_BF16)
+    return fail(PA_ERR_DTYPE, "unknown dtype %d (expected PA_F32, PA_F16 or PA_BF16)", d->dtype);
+  if (d->num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d is negative", d->num_seqs);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PA_ERR_SHAPE, "head counts must be positive (Hq=%d, Hkv=%d)", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "num_blocks (%d) and max_blocks_per_seq (%d) must be positive",
+                d->num_blocks, d->max_blocks_per_seq);
+  if (d->head_dim <= 0 || d->block_size <= 0)
+    return fail(PA_ERR_SHAPE, "head_dim (%d) and block_size (%d) must be positive", d->head_dim,
+                d->block_size);
+  if (d->head_dim != 128 && d->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (128 or 256)", d->head_dim);
+  if (d->block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", d->block_size);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8, 16)", G);
+  if ((int64_t)d->max_blocks_per_seq * pa::kBlockSize > (int64_t)0x3fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq %d exceeds the 2^30-token context limit",
+                d->max_blocks_per_seq);
+  if (d->num_kv_heads > 65535 || d->num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads and num_seqs must be <= 65535 (grid limits)");
+  return ok();
+}
+
+pa_status_t make_plan(const pa_dims_t* d, int64_t max_context_len, int32_t partition_size,
+                      bool need_partition, Plan* pl) {
+  pa_status_t st = check_dims(d);
+  if (st != PA_OK) return st;
+  pl->S = d->num_seqs;
+  pl->Hq = d->num_q_heads;
+  pl->Hkv = d->num_kv_heads;
+  pl->D = d->head_dim;
+  pl->G = d->num_q_heads / d->num_kv_heads;
+  pl->NB = d->num_blocks;
+  pl->MB = d->max_blocks_per_seq;
+  const int64_t cap = (int64_t)d->max_blocks_per_seq * pa::kBlockSize;
+  if (max_context_len > cap)
+    return fail(PA_ERR_SHAPE, "max_context_len %lld exceeds the block-table capacity %lld",
+                (long long)max_context_len, (long long)cap);
+  pl->ctx_bound = max_context_len > 0 ? max_context_len : cap;
+  if (need_partition) {
+    if (partition_size <= 0 || partition_size % pa::kBlockSize)
+      return fail(PA_ERR_PARTITION,
+                  "partition_size %d must be a positive multiple of the block size %d",
+                  partition_size, pa::kBlockSize);
+    pl->P = partition_size;
+    pl->Pmax = (pl->ctx_bound + partition_size - 1) / partition_size;
+    if (pl->Pmax > pa::kMaxReducePartitions)
+      return fail(PA_ERR_UNSUPPORTED, "%lld partitions per sequence exceed the limit %d",
+                  (long long)pl->Pmax, pa::kMaxReducePartitions);
+  } else {
+    // V1: one partition spanning the whole bound, rounded up to whole blocks.
+    pl->P = (int32_t)(((pl->ctx_bound + pa::kBlockSize - 1) / pa::kBlockSize) * pa::kBlockSize);
+    pl->Pmax = 1;
+  }
+  const size_t rows = (size_t)pl->S * pl->Hq * (size_t)pl->Pmax;
+  pl->off_tmp = 0;
+  pl->off_max = align256(rows * pl->D * sizeof(float));
+  pl->off_sum = pl->off_max + align256(rows * sizeof(float));
+  pl->ws_bytes = pl->off_sum + align256(rows * sizeof(float));
+  return ok();
+}
+
+pa_status_t check_tensors(const void* out, const void* q, const void* k, const void* v,
+                          const int32_t* bt, const int32_t* ctx) {
+  if (!out || !q || !k || !v || !bt || !ctx)
+    return fail(PA_ERR_NULL, "a tensor pointer is NULL (out=%p q=%p k=%p v=%p bt=%p ctx=%p)", out,
+                q, k, v, (const void*)bt, (const void*)ctx);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bt) ||
+      !aligned16(ctx))
+    return fail(PA_ERR_ALIGN, "every tensor pointer must be 16-byte aligned");
+  return ok();
+}
+
+pa_status_t check_scale(float scale) {
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
+  return ok();
+}
+
+pa_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+pa::AttnArgs attn_args(const Plan& pl, void* out, const void* q, const void* k, const void* v,
+                       const int32_t* bt, const int32_t* ctx, float scale, void* ws) {
+  pa::AttnArgs a;
+  a.out = out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bt = bt;
+  a.ctx = ctx;
+  char* base = static_cast<char*>(ws);
+  a.tmp_out = base ? reinterpret_cast<float*>(base + pl.off_tmp) : nullptr;
+  a.max_logits = base ? reinterpret_cast<float*>(base + pl.off_max) : nullptr;
+  a.exp_sums = base ? reinterpret_cast<float*>(base + pl.off_sum) : nullptr;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.Hq = pl.Hq;
+  a.Hkv = pl.Hkv;
+  a.NB = pl.NB;
+  a.MB = pl.MB;
+  a.P = pl.P;
+  a.Pmax = (int32_t)pl.Pmax;
+  return a;
+}
+
+pa_status_t run_partition(const pa_dims_t* dims, const Plan& pl, void* out, const void* q,
+                          const void* k, const void* v, const int32_t* bt, const int32_t* ctx,
+                          float scale, void* ws, hipStream_t st) {
+  pa::AttnArgs a = attn_args(pl, out, q, k, v, bt, ctx, scale, ws);
+  return hip_status(pa::launch_attention(dims->dtype, pl.D, pl.G, a, pl.S, st),
+                    "phase-1 attention launch");
+}
+
+pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const int32_t* ctx,
+                       const void* ws, hipStream_t st) {
+  pa::ReduceArgs r;
+  const char* base = static_cast<const char*>(ws);
+  r.out = out;
+  r.ctx = ctx;
+  r.tmp_out = reinterpret_cast<const float*>(base + pl.off_tmp);
+  r.max_logits = reinterpret_cast<const float*>(base + pl.off_max);
+  r.exp_sums = reinterpret_cast<const float*>(base + pl.off_sum);
+  r.Hq = pl.Hq;
+  r.MB = pl.MB;
+  r.P = pl.P;
+  r.Pmax = (int32_t)pl.Pmax;
+  return hip_status(pa::launch_reduce(dims->dtype, pl.D, r, pl.S, st), "phase-2 reduce launch");
+}
+
+// Library-owned workspace, grow-only, one per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+void* g_ws_ptr[kMaxDevices] = {};
+size_t g_ws_size[kMaxDevices] = {};
+
+pa_status_t owned_workspace(size_t bytes, void** out) {
+  int dev = 0;
+  pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_INTERNAL, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (g_ws_size[dev] < bytes) {
+    if (g_ws_ptr[dev]) {
+      st = hip_status(hipFree(g_ws_ptr[dev]), "hipFree(workspace)");
+      g_ws_ptr[dev] = nullptr;
+      g_ws_size[dev] = 0;
+      if (st != PA_OK) return st;
+    }
+    void* p = nullptr;
+    st = hip_status(hipMalloc(&p, bytes), "hipMalloc(workspace)");
+    if (st != PA_OK) return st;
+    g_ws_ptr[dev] = p;
+    g_ws_size[dev] = bytes;
+  }
+  *out = g_ws_ptr[dev];
+  return ok();
+}
+
+int32_t choose(const Plan& pl) {
+  const int64_t t = v1_threshold().load();
+  return pl.ctx_bound <= t ? PA_PATH_V1 : PA_PATH_V2;
+}
+
+pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const void* k,
+                        const void* v, const int32_t* bt, const int32_t* ctx, float scale,
+                        int32_t partition_size, void* stream, void* workspace,
+                        size_t workspace_bytes, bool owned, int64_t max_context_len,
+                        int32_t path) {
+  if (path != PA_PATH_AUTO && path != PA_PATH_V1 && path != PA_PATH_V2)
+    return fail(PA_ERR_SHAPE, "path %d is not PA_PATH_AUTO, PA_PATH_V1 or PA_PATH_V2", path);
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  if (pl.S == 0) return ok();
+  if ((st = check_tensors(out, q, k, v, bt, ctx)) != PA_OK) return st;
+  if ((st = check_scale(scale)) != PA_OK) return st;
+  const int32_t take = path == PA_PATH_AUTO ? choose(pl) : path;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (take == PA_PATH_V1) {
+    Plan p1;
+    if ((st = make_plan(dims, max_context_len, 0, false, &p1)) != PA_OK) return st;
+    return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs);
+  }
+  if (owned) {
+    if ((st = owned_workspace(pl.ws_bytes, &workspace)) != PA_OK) return st;
+  } else {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; V2 needs %zu bytes",
+                                pl.ws_bytes);
+    if (workspace_bytes < pl.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, pl.ws_bytes);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs)) != PA_OK)
+    return st;
+  return run_reduce(dims, pl, out, ctx, workspace, hs);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, int32_t partition_size,
+                      void* stream) {
+  try {
+    return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       partition_size, stream, nullptr, 0, true, 0, PA_PATH_AUTO);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
+                          int32_t partition_size) {
+  Plan pl;
+  if (make_plan(dims, max_context_len, partition_size, true, &pl) != PA_OK) return 0;
+  return pl.ws_bytes;
+}
+
+pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, int32_t partition_size,
+                         void* stream, void* workspace, size_t workspace_bytes,
+                         int64_t max_context_len, int32_t path) {
+  try {
+    return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       partition_size, stream, workspace, workspace_bytes, false,
+                       max_context_len, path);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_v2_partition(const pa_dims_t* dims, void* out, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int32_t partition_size, int64_t max_context_len,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  if (pl.S == 0) return ok();
+  if ((st = check_tensors(out, q, k_cache, v_cache, block_tables, context_lens)) != PA_OK)
+    return st;
+  if ((st = check_scale(scale)) != PA_OK) return st;
+  if (!workspace || workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu needed", workspace,
+                workspace_bytes, pl.ws_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return run_partition(dims, pl, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       workspace, static_cast<hipStream_t>(stream));
+}
+
+pa_status_t pa_v2_reduce(const pa_dims_t* dims, void* out, const int32_t* context_lens,
+                         int32_t partition_size, int64_t max_context_len,
+                         const void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  if (pl.S == 0) return ok();
+  if (!out || !context_lens) return fail(PA_ERR_NULL, "out or context_lens is NULL");
+  if (!aligned16(out) || !aligned16(context_lens))
+    return fail(PA_ERR_ALIGN, "every tensor pointer must be 16-byte aligned");
+  if (!workspace || workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu needed", workspace,
+                workspace_bytes, pl.ws_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return run_reduce(dims, pl, out, context_lens, workspace, static_cast<hipStream_t>(stream));
+}
+
+pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, float scale, int64_t max_context_len,
+                  void* stream) {
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, 0, false, &pl);
+  if (st != PA_OK) return st;
+  if (pl.S == 0) return ok();
+  if ((st = check_tensors(out, q, k_cache, v_cache, block_tables, context_lens)) != PA_OK)
+    return st;
+  if ((st = check_scale(scale)) != PA_OK) return st;
+  return run_partition(dims, pl, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       nullptr, static_cast<hipStream_t>(stream));
+}
+
+int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len) {
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, 0, false, &pl);
+  if (st != PA_OK) return st;
+  return choose(pl);
+}
+
+void pa_set_v1_max_context(int64_t tokens) { v1_threshold().store(tokens < 0 ? 0 : tokens); }
+
+int64_t pa_get_v1_max_context(void) { return v1_threshold().load(); }
+
+int64_t pa_num_partitions(int64_t n, int32_t partition_size) {
+  if (n < 0 || partition_size <= 0) return -1;
+  return (n + partition_size - 1) / partition_size;
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+void pa_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = -1;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (!g_ws_ptr[d]) continue;
+    if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws_ptr[d]);
+    g_ws_ptr[d] = nullptr;
+    g_ws_size[d] = 0;
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+const char* pa_version(void) { return "pa_decode 0.1.0 gfx950"; }
+
+pa_status_t pa_set_mfma_variant(int32_t variant) {
+  if (pa::set_mfma_variant(variant) != 0)
+    return fail(PA_ERR_UNSUPPORTED, "matrix-core variant %d unknown (0, 1 or 2)", variant);
+  return ok();
+}
+
+int32_t pa_get_mfma_variant(void) { return pa::get_mfma_variant(); }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI front end (pa_api.hip) and the
+// kernels (pa_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;   // tokens per KV-cache block
+constexpr int kWaves = 4;        // waves per attention work-group
+constexpr int kMaxReducePartitions = 8192;  // phase-2 weights live in LDS (32 KB)
+
+// Arguments of the attention kernel (phase 1 and V1 share it).
+struct AttnArgs {
+  void* out;                 // [S, Hq, D] element type of q
+  const void* q;             // [S, Hq, D]
+  const void* k;             // [NB, Hkv, 16, D]
+  const void* v;             // [NB, Hkv, 16, D]
+  const int32_t* bt;         // [S, MB]
+  const int32_t* ctx;        // [S]
+  float* tmp_out;            // [S, Hq, Pmax, D] (unused when Pmax == 1)
+  float* max_logits;         // [S, Hq, Pmax]
+  float* exp_sums;           // [S, Hq, Pmax]
+  float scale_log2;          // scale * log2(e)
+  int32_t Hq, Hkv, NB, MB;
+  int32_t P;                 // tokens per partition (multiple of 16)
+  int32_t Pmax;              // partition-grid size
+};
+
+// Arguments of the phase-2 (cross-partition) kernel.
+struct ReduceArgs {
+  void* out;
+  const int32_t* ctx;
+  const float* tmp_out;
+  const float* max_logits;
+  const float* exp_sums;
+  int32_t Hq, MB, P, Pmax;
+};
+
+// Work-group shape of the matrix-core kernel (0, 1 or 2; see pa_kernels.hip).
+// set_mfma_variant returns -1 for an unknown variant.
+int set_mfma_variant(int v);
+int get_mfma_variant();
+
+// Kernel family chosen for a (dtype, G) pair.
+enum class Kernel { kMfma, kValu };
+Kernel kernel_for(int dtype, int group);
+
+// Launch the attention kernel on grid (Pmax, Hkv, S).  Returns the launch status.
+hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
+                            hipStream_t stream);
+// Launch the phase-2 kernel on grid (S*Hq, D/32).
+hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
+                         hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,837 @@
+// HIP kernels of the paged split-KV decode path, written for CDNA4 (gfx950).
+//
+// Phase 1 / V1 ("Phase 1: Per-partition attention", project_6 commit 96f4baf
+// page, V2 plan): one work-group per (partition, KV head, sequence).  The
+// work-group holds every query head of its GQA group, so each K/V byte is
+// read from HBM once for all of them.  Its 4 waves take the partition's
+// 16-token cache blocks in turn; each wave keeps a running (max, sum,
+// unnormalised output) per head -- the online softmax, i.e. the
+// flash-attention tiling the page names -- and the 4 partial states are
+// merged through LDS at the end with the same log-sum-exp rule Phase 2 uses.
+//
+// Two inner loops:
+//   * attn_mfma_kernel (fp16 / bf16, G >= 4): QK^T and PV are small dense
+//     contractions over the head group, done on the matrix cores.
+//     QK^T: v_mfma_f32_16x16x32_{bf16,f16}, A = the 16 keys of a block
+//     (rows = tokens), B = the group's queries (columns = heads, padded to
+//     16).  The result lands with column = head, rows = tokens, which is
+//     exactly the A-operand layout of PV: v_mfma_f32_16x16x16 with
+//     A = probabilities (rows = heads, k = tokens) and B = V (k = tokens).
+//     Each lane loads V rows as 16-byte runs of 8 columns and feeds column
+//     j of its run to PV instruction j, so no transpose through LDS is
+//     needed: column n of instruction j is head-dim index 8n + j.
+//   * attn_valu_kernel (fp32, or G < 4): plain fp32 FMAs; the query group is
+//     staged in LDS and the probabilities of a block are exchanged through
+//     a per-wave LDS slot.
+//
+// Phase 2 ("Phase 2: Cross-partition reduction (log-sum-exp)", same page):
+// reduce_kernel, one work-group per (sequence, head, 32 columns).
+//
+// Exponentials use v_exp_f32 (base 2) on logits pre-scaled by
+// scale * log2(e); max logits are stored back in natural-log units.  All
+// accumulation is fp32.  Tail tokens of the last block are excluded by
+// selecting -inf logits and zero V rows (never by multiplying by zero, so
+// stale NaN/Inf in unused cache slots cannot leak into the result).
+
+#include <atomic>
+#include <cstdlib>
+
+#include "pa_internal.h"
+#include "pa_decode.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = kWaves * 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.442695040888963407360f;
+// Base-2 headroom a block max may exceed the running reference max by before the
+// accumulators are rescaled (probabilities stay below 2^8, far from fp32 limits).
+constexpr float kRescaleSlack = 8.f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- element conversions -------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  if constexpr (DT == PA_BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <int DT>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  if constexpr (DT == PA_BF16) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+template <int DT>
+__device__ __forceinline__ uint32_t to_bits16(float x) {
+  if constexpr (DT == PA_BF16) return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+  else return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return to_bits16<DT>(lo) | (to_bits16<DT>(hi) << 16);
+}
+
+// Store n (4 or 8) consecutive fp32 values as element type DT at element offset idx.
+template <int DT, int N>
+__device__ __forceinline__ void store_out(void* out, size_t idx, const float* v) {
+  static_assert(N == 2 || N == 4 || N == 8, "");
+  if constexpr (DT == PA_F32) {
+    float* o = static_cast<float*>(out) + idx;
+    if constexpr (N == 2) {
+      *reinterpret_cast<f32x2*>(o) = f32x2{v[0], v[1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 4)
+        *reinterpret_cast<f32x4*>(o + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    }
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(out) + idx;
+    if constexpr (N == 2) {
+      *reinterpret_cast<uint32_t*>(o) = pack2<DT>(v[0], v[1]);
+    } else if constexpr (N == 4) {
+      *reinterpret_cast<u32x2*>(o) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+    } else {
+      *reinterpret_cast<u32x4*>(o) = u32x4{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]),
+                                           pack2<DT>(v[4], v[5]), pack2<DT>(v[6], v[7])};
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_f32(float* dst, const float* v) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4)
+    *reinterpret_cast<f32x4*>(dst + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+}
+
+// ---- matrix-core wrappers -------------------------------------------------------------
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// ---- work-group set-up shared by both attention kernels ------------------------------
+struct Part {
+  int n;       // context length (clamped to the table capacity)
+  int nparts;  // partitions of this sequence that exist in the grid
+  int tok0;    // first token of this partition
+  int ntok;    // tokens in this partition
+  int nblk;    // cache blocks in this partition
+};
+
+__device__ __forceinline__ Part plan_partition(const AttnArgs& a, int b, int p) {
+  Part r;
+  int n = a.ctx[b];
+  const int cap = a.MB * kBlockSize;
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  int np = (n + a.P - 1) / a.P;
+  r.n = n;
+  r.nparts = np > a.Pmax ? a.Pmax : np;
+  r.tok0 = p * a.P;
+  r.ntok = min(a.P, n - r.tok0);
+  r.nblk = (r.ntok + kBlockSize - 1) / kBlockSize;
+  return r;
+}
+
+// A sequence with no cached tokens attends to nothing: its output is 0.
+template <int DT, int D, int G>
+__device__ __forceinline__ void write_zero_group(const AttnArgs& a, int b, int g) {
+  const size_t base = ((size_t)b * a.Hq + (size_t)g * G) * D;
+  const float z[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int idx = threadIdx.x * 4; idx < G * D; idx += blockDim.x * 4)
+    store_out<DT, 4>(a.out, base + idx, z);
+}
+
+// =======================================================================================
+// Matrix-core attention kernel: fp16 / bf16, G in {4, 8, 16}.
+//
+// NW waves per work-group share one partition (wave w takes blocks w, w+NW, ...).
+// Each wave runs an NBUF-deep software pipeline in registers: while it computes
+// block k, the loads of blocks k+1 .. k+NBUF-1 are in flight.  At head_dim 128
+// the register budget is 2 waves per SIMD (256 VGPRs), which keeps every
+// work-group of the 100K-token / 4-KV-head shape (784 of them) resident at once
+// for NW <= 2.  At head_dim 256 a block is twice the registers and the budget is
+// one wave per SIMD.
+// =======================================================================================
+template <int DT, int D, int G, int NW, int NBUF>
+__global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(const AttnArgs a) {
+  static_assert(DT == PA_BF16 || DT == PA_F16, "matrix-core path is 16-bit only");
+  static_assert(G >= 1 && G <= 16, "head group must fit the 16 MFMA columns");
+  static_assert(NBUF >= 2, "need at least one block in flight");
+  constexpr bool kBF = DT == PA_BF16;
+  constexpr int NKK = D / 32;    // QK^T instructions per block (k = 32 head-dim columns each)
+  constexpr int NC = D / 128;    // 16-byte V runs per lane per row
+  constexpr int NMM = D / 16;    // PV instructions per block (16 head-dim columns each)
+
+  __shared__ u32x4 s_qf[NKK][64];   // query operand, one 16-byte fragment per lane
+  __shared__ float s_mref[NW][16];  // per wave and head: reference max of the sums
+  __shared__ float s_mmax[NW][16];  // per wave and head: true max logit
+  __shared__ float s_l[NW][16];     // per wave and head: exp-sum relative to the reference
+  __shared__ float s_o[NW > 1 ? NW - 1 : 1][NMM * 4][64];
+
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;  // token row (K loads), head column (Q, S), V column run
+  const int kg = lane >> 4;   // k-group of the MFMA operands
+
+  const Part pt = plan_partition(a, b, p);
+  if (p >= pt.nparts) {
+    if (p == 0) write_zero_group<DT, D, G>(a, b, g);
+    return;
+  }
+  const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
+
+  // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
+  // pad the group to 16 heads).  Kept in LDS in lane order: conflict-free 16-byte reads.
+  if (w == 0) {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G + r16) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s_qf[kk][lane] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
+                               : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const size_t hstride = (size_t)kBlockSize * D;
+  const size_t bstride = (size_t)a.Hkv * hstride;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (size_t)g * hstride;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + (size_t)g * hstride;
+  __syncthreads();
+
+  f32x4 O[NMM];
+#pragma unroll
+  for (int mm = 0; mm < NMM; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Online softmax of head r16 in base-2 units.  The sums are kept relative to a
+  // reference m_ref that only moves when a block max exceeds it by more than
+  // kRescaleSlack, so accumulator rescaling is rare; m_max tracks the true max.
+  float m_ref = kNegInf, m_max = kNegInf;
+  float l_run = 0.f;  // this lane's share of the exp-sum of head r16
+  int btv = 0;        // block ids of the current 64-block chunk, one per lane
+
+  u32x4 kbuf[NBUF][NKK], vbuf[NBUF][NC][4];
+
+  auto load_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
+    int phys = __builtin_amdgcn_readlane(btv, kidx);
+    if ((unsigned)phys >= (unsigned)a.NB) phys = 0;
+    const uint16_t* kb = kbase + (size_t)phys * bstride;
+    const uint16_t* vb = vbase + (size_t)phys * bstride;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      kr[kk] = *reinterpret_cast<const u32x4*>(kb + r16 * D + 32 * kk + 8 * kg);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vr[c][i] = *reinterpret_cast<const u32x4*>(vb + (4 * kg + i) * D + 128 * c + 8 * r16);
+  };
+
+  auto compute_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
+    // S^T = K Q^T: lane (r16, kg) gets tokens 4*kg + i of head r16.  The query
+    // fragments are re-read from LDS every block rather than pinned in registers;
+    // the opaque lane index keeps the compiler from hoisting the reads.
+    int ql = lane;
+    asm volatile("" : "+v"(ql));
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = mfma_16x16x32<kBF>(kr[kk], s_qf[kk][ql], s);
+    const int valid = pt.ntok - (w + NW * kidx) * kBlockSize;  // >= 1, wave-uniform
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * kg + i < valid) ? s[i] * a.scale_log2 : kNegInf;
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    m_max = fmaxf(m_max, bm);
+    if (__any(bm > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, bm);
+      const float alpha = m_ref == kNegInf ? 0.f : exp2_fast(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      // Accumulator rows are heads 4*kg + i; fetch their factors from lanes 0..15.
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+      for (int mm = 0; mm < NMM; ++mm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[mm][i] *= al[i];
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = x[i] == kNegInf ? 0.f : exp2_fast(x[i] - m_ref);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const u32x2 pa = u32x2{pack2<DT>(pr[0], pr[1]), pack2<DT>(pr[2], pr[3])};
+    if (valid < kBlockSize) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * kg + i >= valid) vr[c][i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // O += P V: instruction 8c + j uses column j of every lane's 8-column run.
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 bv = u32x2{__builtin_amdgcn_perm(vr[c][1][j >> 1], vr[c][0][j >> 1], sel),
+                               __builtin_amdgcn_perm(vr[c][3][j >> 1], vr[c][2][j >> 1], sel)};
+        O[8 * c + j] = mfma_16x16x16<kBF>(pa, bv, O[8 * c + j]);
+      }
+  };
+
+  // Blocks are taken 64 at a time (one block id per lane).  Inside a chunk the NBUF
+  // register buffers rotate; every stage issues the loads of the block NBUF-1 ahead
+  // (the index is clamped to the chunk's last block, so the loads are unconditional,
+  // the compiler's wait counts stay exact and the prefetch overlaps the compute).
+  for (int c0 = 0; c0 < kcount; c0 += 64) {
+    const int cnt = min(64, kcount - c0);
+    btv = lane < cnt ? btrow[w + NW * (c0 + lane)] : 0;
+    const int last = cnt - 1;
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) load_block(kbuf[s], vbuf[s], min(s, last));
+    for (int k = 0; k < cnt; k += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        const int nb = (s + NBUF - 1) % NBUF;
+        load_block(kbuf[nb], vbuf[nb], min(k + s + NBUF - 1, last));
+        // Keep the scheduler from interleaving the next block's loads with this
+        // block's math: that would stretch live ranges past the register budget.
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + s >= cnt) break;
+        compute_block(kbuf[s], vbuf[s], c0 + k + s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- merge the NW waves' states (log-sum-exp) ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (kg == 0) {
+    s_mref[w][r16] = m_ref;
+    s_mmax[w][r16] = m_max;
+    s_l[w][r16] = l_run;
+  }
+  if (NW > 1 && w > 0) {
+#pragma unroll
+    for (int mm = 0; mm < NMM; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[w - 1][mm * 4 + i][lane] = O[mm][i];
+  }
+  __syncthreads();
+  if (w != 0) return;
+
+  // Per head h: true partition max Mt, wave factors exp2(m_ref_w - Mt) and the exp-sum
+  // L = sum_t exp2(x_t - Mt) of the whole partition.
+  auto head_stats = [&](int h, float (&fac)[NW], float& Mt, float& L) {
+    Mt = s_mmax[0][h];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) Mt = fmaxf(Mt, s_mmax[ww][h]);
+    L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mw = s_mref[ww][h];
+      fac[ww] = mw == kNegInf ? 0.f : exp2_fast(mw - Mt);
+      L += fac[ww] * s_l[ww][h];
+    }
+  };
+
+  const bool single = pt.nparts == 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    if (h >= G) continue;
+    float fac[NW], Mt, L;
+    head_stats(h, fac, Mt, L);
+    const float linv = 1.f / L;
+    const size_t qh = (size_t)b * a.Hq + (size_t)g * G + h;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float vals[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = (8 * c + j) * 4 + i;
+        float o = fac[0] * O[8 * c + j][i];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) o += fac[ww] * s_o[ww - 1][e][lane];
+        vals[j] = o * linv;
+      }
+      const int d0 = 128 * c + 8 * r16;
+      if (single)
+        store_out<DT, 8>(a.out, qh * D + d0, vals);
+      else
+        store_f32<8>(a.tmp_out + (qh * a.Pmax + p) * D + d0, vals);
+    }
+  }
+  if (!single && kg == 0 && r16 < G) {
+    float fac[NW], Mt, L;
+    head_stats(r16, fac, Mt, L);
+    const size_t idx = ((size_t)b * a.Hq + (size_t)g * G + r16) * a.Pmax + p;
+    a.max_logits[idx] = Mt * kLn2;
+    a.exp_sums[idx] = L;
+  }
+}
+
+// =======================================================================================
+// Vector-ALU attention kernel: any element type, any supported G.
+// =======================================================================================
+template <int B> struct Bytes;
+template <> struct Bytes<4> { typedef uint32_t T; };
+template <> struct Bytes<8> { typedef u32x2 T; };
+template <> struct Bytes<16> { typedef u32x4 T; };
+
+// Element e (0-based) of a register run holding elements of type DT.
+template <int DT, typename V>
+__device__ __forceinline__ float elem(const V& v, int e) {
+  if constexpr (DT == PA_F32) {
+    if constexpr (sizeof(V) == 4) return __uint_as_float(v);
+    else return __uint_as_float(v[e]);
+  } else {
+    uint32_t word;
+    if constexpr (sizeof(V) == 4) word = v;
+    else word = v[e >> 1];
+    return (e & 1) ? half_hi<DT>(word) : half_lo<DT>(word);
+  }
+}
+
+template <int DT, int D, int G>
+__global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
+  constexpr int ES = DT == PA_F32 ? 4 : 2;
+  constexpr int ROWB = D * ES;   // bytes per cache row
+  constexpr int KCH = ROWB / 64; // 16-byte K chunks per lane (a row is split over 4 lanes)
+  constexpr int EPC = 16 / ES;   // elements per 16-byte chunk
+  constexpr int VE = D / 64;     // V columns per lane
+  constexpr int VB = VE * ES;    // V bytes per lane per row
+  typedef typename Bytes<VB>::T VT;
+  constexpr int kQBytes = G * D * 4;
+  constexpr int kPBytes = kWaves * 16 * G * 4;
+  constexpr int kOBytes = (kWaves - 1) * G * VE * 64 * 4;
+  constexpr int kSmem = (kQBytes + kPBytes) > kOBytes ? (kQBytes + kPBytes) : kOBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  __shared__ float s_mref[kWaves][G];
+  __shared__ float s_mmax[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  float* s_q = reinterpret_cast<float*>(smem);             // [G][D]   during the loop
+  float* s_p = reinterpret_cast<float*>(smem + kQBytes);   // [kWaves][16][G]
+  float* s_o = reinterpret_cast<float*>(smem);             // [kWaves-1][G*VE][64] after it
+
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int t = lane >> 2, r = lane & 3;
+
+  const Part pt = plan_partition(a, b, p);
+  if (p >= pt.nparts) {
+    if (p == 0) write_zero_group<DT, D, G>(a, b, g);
+    return;
+  }
+  const int kcount = w < pt.nblk ? (pt.nblk - w + kWaves - 1) / kWaves : 0;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
+
+  // Stage the head group's queries, pre-multiplied by scale*log2(e), as fp32.
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const size_t src = ((size_t)b * a.Hq + (size_t)g * G) * D + idx;
+    float qv;
+    if constexpr (DT == PA_F32) qv = static_cast<const float*>(a.q)[src];
+    else qv = half_lo<DT>(static_cast<const uint16_t*>(a.q)[src]);
+    s_q[idx] = qv * a.scale_log2;
+  }
+
+  int btv = 0;
+  const size_t hstride = (size_t)kBlockSize * ROWB;   // bytes per (block, head)
+  const size_t bstride = (size_t)a.Hkv * hstride;
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + (size_t)g * hstride;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + (size_t)g * hstride;
+  __syncthreads();
+
+  float O[G][VE];
+  float m_ref[G], m_max[G], l_run[G];  // see attn_mfma_kernel; wave-uniform per head
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_ref[h] = kNegInf;
+    m_max[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) O[h][e] = 0.f;
+  }
+
+  u32x4 kA[KCH], kB[KCH];
+  VT vA[16], vB[16];
+
+  auto load_block = [&](u32x4 (&kr)[KCH], VT (&vr)[16], int kidx) {
+    int phys = __builtin_amdgcn_readlane(btv, kidx & 63);
+    if ((unsigned)phys >= (unsigned)a.NB) phys = 0;
+    const unsigned char* kb = kbase + (size_t)phys * bstride;
+    const unsigned char* vb = vbase + (size_t)phys * bstride;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j)
+      kr[j] = *reinterpret_cast<const u32x4*>(kb + t * ROWB + (r + 4 * j) * 16);
+#pragma unroll
+    for (int t2 = 0; t2 < 16; ++t2)
+      vr[t2] = *reinterpret_cast<const VT*>(vb + t2 * ROWB + lane * VB);
+  };
+
+  auto compute_block = [&](u32x4 (&kr)[KCH], VT (&vr)[16], int kidx) {
+    float acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int d0 = (r + 4 * j) * EPC;
+#pragma unroll
+      for (int e4 = 0; e4 < EPC; e4 += 4) {
+        float kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = elem<DT>(kr[j], e4 + e);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(s_q + h * D + d0 + e4);
+          acc[h] += qv[0] * kv[0] + qv[1] * kv[1] + qv[2] * kv[2] + qv[3] * kv[3];
+        }
+      }
+    }
+    const int valid = pt.ntok - (w + kWaves * kidx) * kBlockSize;  // >= 1, wave-uniform
+    bool move = false;
+    float x[G], bm[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sv = acc[h];
+      sv += __shfl_xor(sv, 1);
+      sv += __shfl_xor(sv, 2);
+      x[h] = t < valid ? sv : kNegInf;
+      float v = x[h];
+      v = fmaxf(v, __shfl_xor(v, 4));
+      v = fmaxf(v, __shfl_xor(v, 8));
+      v = fmaxf(v, __shfl_xor(v, 16));
+      v = fmaxf(v, __shfl_xor(v, 32));
+      bm[h] = v;
+      m_max[h] = fmaxf(m_max[h], v);
+      move |= v > m_ref[h] + kRescaleSlack;
+    }
+    if (move) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float m_new = fmaxf(m_ref[h], bm[h]);
+        const float alpha = m_ref[h] == kNegInf ? 0.f : exp2_fast(m_ref[h] - m_new);
+        m_ref[h] = m_new;
+        l_run[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) O[h][e] *= alpha;
+      }
+    }
+    float* pw = s_p + w * 16 * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ph = x[h] == kNegInf ? 0.f : exp2_fast(x[h] - m_ref[h]);
+      if (r == 0) {
+        l_run[h] += ph;
+        pw[t * G + h] = ph;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t2 = 0; t2 < 16; ++t2) {
+      if (t2 < valid) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ph = pw[t2 * G + h];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) O[h][e] += ph * elem<DT>(vr[t2], e);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Blocks are taken 64 at a time (one block id per lane).  Inside a chunk two
+  // register buffers alternate; the next block's loads are always issued (the index
+  // is clamped to the chunk's last block) so the compiler's wait counts stay exact
+  // and the prefetch overlaps the FMAs.
+  for (int c0 = 0; c0 < kcount; c0 += 64) {
+    const int cnt = min(64, kcount - c0);
+    btv = lane < cnt ? btrow[w + kWaves * (c0 + lane)] : 0;
+    const int last = cnt - 1;
+    load_block(kA, vA, 0);
+    for (int k = 0; k < cnt; k += 2) {
+      load_block(kB, vB, min(k + 1, last));
+      compute_block(kA, vA, c0 + k);
+      if (k + 1 >= cnt) break;
+      load_block(kA, vA, min(k + 2, last));
+      compute_block(kB, vB, c0 + k + 1);
+    }
+  }
+
+  // Full-wave exp-sum per head (only lanes with r == 0 accumulated).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float l = l_run[h];
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) l += __shfl_xor(l, s);
+    l_run[h] = l;
+  }
+  __syncthreads();  // every wave is done with s_q / s_p; their bytes become s_o
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_mref[w][h] = m_ref[h];
+      s_mmax[w][h] = m_max[h];
+      s_l[w][h] = l_run[h];
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s_o[((w - 1) * G * VE + h * VE + e) * 64 + lane] = O[h][e];
+  }
+  __syncthreads();
+  if (w != 0) return;
+
+  const bool single = pt.nparts == 1;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float Mt = s_mmax[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) Mt = fmaxf(Mt, s_mmax[ww][h]);
+    float fac[kWaves], L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = s_mref[ww][h];
+      fac[ww] = mw == kNegInf ? 0.f : exp2_fast(mw - Mt);
+      L += fac[ww] * s_l[ww][h];
+    }
+    const float linv = 1.f / L;
+    float vals[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float o = fac[0] * O[h][e];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww)
+        o += fac[ww] * s_o[((ww - 1) * G * VE + h * VE + e) * 64 + lane];
+      vals[e] = o * linv;
+    }
+    const size_t qh = (size_t)b * a.Hq + (size_t)g * G + h;
+    if (single) {
+      store_out<DT, VE>(a.out, qh * D + lane * VE, vals);
+    } else {
+      float* dst = a.tmp_out + (qh * a.Pmax + p) * D + lane * VE;
+      if constexpr (VE == 2) *reinterpret_cast<f32x2*>(dst) = f32x2{vals[0], vals[1]};
+      else store_f32<VE>(dst, vals);
+      if (lane == 0) {
+        a.max_logits[qh * a.Pmax + p] = Mt * kLn2;
+        a.exp_sums[qh * a.Pmax + p] = L;
+      }
+    }
+  }
+}
+
+// =======================================================================================
+// Phase 2: cross-partition log-sum-exp merge.
+// Grid (S*Hq, D/32); 256 threads = 32 partition lanes x 8 float4 columns.
+// =======================================================================================
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s);
+  return v;
+}
+
+template <int DT, int D>
+__global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
+  extern __shared__ float s_w[];  // [Pmax] rescaled exp-sums r_p
+  __shared__ float s_red[4];
+  __shared__ f32x4 s_acc[32][8];
+  const int bh = blockIdx.x, chunk = blockIdx.y;
+  const int b = bh / a.Hq;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+
+  int n = a.ctx[b];
+  const int cap = a.MB * kBlockSize;
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  int nparts = (n + a.P - 1) / a.P;
+  if (nparts > a.Pmax) nparts = a.Pmax;
+  if (nparts <= 1) return;  // phase 1 wrote the final output (or zeros)
+
+  const size_t base = (size_t)bh * a.Pmax;
+  float mx = kNegInf;
+  for (int q = tid; q < nparts; q += 256) mx = fmaxf(mx, a.max_logits[base + q]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[w] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int q = tid; q < nparts; q += 256) {
+    const float rq = exp2_fast((a.max_logits[base + q] - M) * kLog2e) * a.exp_sums[base + q];
+    s_w[q] = rq;
+    sum += rq;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[w] = sum;
+  __syncthreads();
+  const float inv = 1.f / ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
+
+  const int d4 = tid & 7, pg = tid >> 3;
+  const float* src = a.tmp_out + base * D + chunk * 32 + d4 * 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int q = pg; q < nparts; q += 32)
+    acc += s_w[q] * *reinterpret_cast<const f32x4*>(src + (size_t)q * D);
+  s_acc[pg][d4] = acc;
+  __syncthreads();
+  if (tid < 8) {
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 32; ++q) tot += s_acc[q][tid];
+    const float vals[4] = {tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
+    store_out<DT, 4>(a.out, (size_t)bh * D + chunk * 32 + tid * 4, vals);
+  }
+}
+
+// ---- dispatch --------------------------------------------------------------------------
+// Work-group shape of the matrix-core kernel (see attn_mfma_kernel):
+//   0 = 2 waves, pipeline depth 3 (head_dim 128) / 2 (head_dim 256)  [default]
+//   1 = 1 wave,  pipeline depth 5 / 3
+//   2 = 4 waves, pipeline depth 2
+std::atomic<int> g_mfma_variant{-1};
+
+int mfma_variant() {
+  int v = g_mfma_variant.load(std::memory_order_relaxed);
+  if (v < 0) {
+    v = 0;
+    const char* e = std::getenv("PA_MFMA_VARIANT");
+    if (e && (e[0] == '0' || e[0] == '1' || e[0] == '2') && e[1] == '\0') v = e[0] - '0';
+    g_mfma_variant.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int DT, int D, int G>
+hipError_t launch_attn_t(const AttnArgs& a, int S, hipStream_t st) {
+  dim3 grid(a.Pmax, a.Hkv, S);
+  if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
+    switch (mfma_variant()) {
+      case 0:
+        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>), grid,
+                           dim3(2 * 64), 0, st, a);
+        break;
+      case 1:
+        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>), grid,
+                           dim3(64), 0, st, a);
+        break;
+      default:
+        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 4, 2>), grid, dim3(4 * 64), 0, st, a);
+        break;
+    }
+  } else {
+    hipLaunchKernelGGL((attn_valu_kernel<DT, D, G>), grid, dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_attn_g(int G, const AttnArgs& a, int S, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_attn_t<DT, D, 1>(a, S, st);
+    case 2: return launch_attn_t<DT, D, 2>(a, S, st);
+    case 4: return launch_attn_t<DT, D, 4>(a, S, st);
+    case 8: return launch_attn_t<DT, D, 8>(a, S, st);
+    case 16: return launch_attn_t<DT, D, 16>(a, S, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_attn_d(int D, int G, const AttnArgs& a, int S, hipStream_t st) {
+  if (D == 128) return launch_attn_g<DT, 128>(G, a, S, st);
+  if (D == 256) return launch_attn_g<DT, 256>(G, a, S, st);
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
+  dim3 block(256);
+  const size_t shmem = (size_t)a.Pmax * sizeof(float);
+  if (D == 128) {
+    dim3 grid((unsigned)(S * a.Hq), 128 / 32);
+    hipLaunchKernelGGL((reduce_kernel<DT, 128>), grid, block, shmem, st, a);
+  } else if (D == 256) {
+    dim3 grid((unsigned)(S * a.Hq), 256 / 32);
+    hipLaunchKernelGGL((reduce_kernel<DT, 256>), grid, block, shmem, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int set_mfma_variant(int v) {
+  if (v < 0 || v > 2) return -1;
+  g_mfma_variant.store(v, std::memory_order_relaxed);
+  return 0;
+}
+
+int get_mfma_variant() { return mfma_variant(); }
+
+Kernel kernel_for(int dtype, int group) {
+  return (dtype != PA_F32 && group >= 4) ? Kernel::kMfma : Kernel::kValu;
+}
+
+hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
+                            hipStream_t stream) {
+  switch (dtype) {
+    case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, a, num_seqs, stream);
+    case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, a, num_seqs, stream);
+    case PA_BF16: return launch_attn_d<PA_BF16>(head_dim, group, a, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
+                         hipStream_t stream) {
+  switch (dtype) {
+    case PA_F32: return launch_reduce_d<PA_F32>(head_dim, a, num_seqs, stream);
+    case PA_F16: return launch_reduce_d<PA_F16>(head_dim, a, num_seqs, stream);
+    case PA_BF16: return launch_reduce_d<PA_BF16>(head_dim, a, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa
