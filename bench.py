@@ -28,6 +28,25 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+KERNEL_SOURCE = os.path.join(ROOT, "paged_split_kv_pa_amd", "csrc", "pa_kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_long_100k_hbm_traffic.md")
+
+
+def counted_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None
+    when the kernel source has changed since those counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        fields = dict(ln.split(": ", 1) for ln in text.splitlines() if ": " in ln
+                      and ln.split(": ", 1)[0] in ("traffic_bytes_per_launch",
+                                                    "kernel_source_sha256_prefix"))
+        digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if digest.startswith(fields["kernel_source_sha256_prefix"].strip()):
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
 
 
 def log(msg):
@@ -47,7 +66,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference "
+                         "kernel for scaling hardware byte counters), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib, reps=5):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate the
+    byte counters read for the decode kernels (bytes expected / bytes counted)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": reps}), flush=True)
 
 
 def to_dev(a, dtype):
@@ -76,7 +111,7 @@ def cpu_baseline(w, seconds):
                                       w.context_lens, w.scale, w.dtype)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= seconds or runs >= 50:
+        if el >= seconds:
             break
     if ctx is not None:
         ctx.restore_original_limits()
@@ -93,6 +128,10 @@ def main():
               "kernel is measured at one GPU's share of the work", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     from paged_split_kv_pa_amd import binding as B
     from paged_split_kv_pa_amd import workloads as wl
@@ -121,21 +160,41 @@ def main():
     path = B.pa_choose_path(B.dims_of(q, kc0, bt))
     stream = torch.cuda.current_stream()
 
+    # Argument tuples are marshalled once, so a step costs two plain C calls on the
+    # host (the GPU, not Python, must be what bounds the timed loop).
+    import ctypes
+    lib = B.lib()
+    dims = B.dims_of(q, kc0, bt)
+    dref = ctypes.byref(dims)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    wsb = ws.numel()
+    scale = ctypes.c_float(w.scale)
+    # One C call per step: pa_decode_profiled = pa_decode_ex (same kernels, same
+    # workspace, same path) plus start/stop timestamps of the attention kernel taken
+    # by the runtime at dispatch and completion.
+    call_args = [[dref, vp(out), vp(q), vp(ks[c]), vp(vs[c]), vp(bt), vp(ctx), scale, P, sptr,
+                  vp(ws), wsb, 0, path, None, None] for c in range(R)]
+
+    # HIP events through the runtime torch already loaded (one runtime per process):
+    # recording them costs far less host time than torch.cuda.Event.
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+
+    def new_event():
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
     def step(i, ev0=None, ev1=None):
-        k, v = ks[i % R], vs[i % R]
-        if path == B.PA_PATH_V1:
-            if ev0 is not None:
-                ev0.record(stream)
-            B.pa_v1(out, q, k, v, bt, ctx, w.scale)
-            if ev1 is not None:
-                ev1.record(stream)
-            return
-        if ev0 is not None:
-            ev0.record(stream)
-        B.pa_v2_partition(out, q, k, v, bt, ctx, w.scale, ws, P)
-        if ev1 is not None:
-            ev1.record(stream)
-        B.pa_v2_reduce(out, q, k, bt, ctx, ws, P)
+        a = call_args[i % R]
+        a[14], a[15] = ev0, ev1
+        st = lib.pa_decode_profiled(*a)
+        if st != 0:
+            raise B.PaError(st, B.pa_last_error())
 
     # First step: its output is kept and checked against the oracle in the CPU leg.
     step(0)
@@ -147,20 +206,28 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev0 = [new_event() for _ in range(args.steps)]
+    ev1 = [new_event() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, ev0[i], ev1[i])
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k1 = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]  # us, phase-1 launch
+    ms = ctypes.c_float()
+    k1 = []
+    for a, b in zip(ev0, ev1):
+        hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        k1.append(ms.value * 1e3)  # us, attention kernel (phase 1)
+    for e in ev0 + ev1:
+        hip.hipEventDestroy(e)
     ms_per_step = wall * 1e3 / args.steps
+    enqueue_us = (t_enq - t0) * 1e6 / args.steps
     k1_mean = float(np.mean(k1))
-    log(f"step {ms_per_step * 1e3:.2f} us; phase-1 kernel mean {k1_mean:.2f} us "
-        f"(median {np.median(k1):.2f}, p10 {np.percentile(k1, 10):.2f}, "
-        f"p90 {np.percentile(k1, 90):.2f})")
+    log(f"step {ms_per_step * 1e3:.2f} us (host enqueue {enqueue_us:.2f} us/step); attention "
+        f"kernel mean {k1_mean:.2f} us (median {np.median(k1):.2f}, p10 "
+        f"{np.percentile(k1, 10):.2f}, p90 {np.percentile(k1, 90):.2f})")
 
     value = kvb / (ms_per_step / 1e3) / 1e9
     achieved = kvb / (k1_mean / 1e6) / 1e9
@@ -190,9 +257,11 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counted_traffic() if args.config == 2 and P == 512 else None,
             "kernel": "attn_mfma_kernel (phase 1)", "kernel_mean_us": round(k1_mean, 3),
         },
+        "host_enqueue_us_per_step": round(enqueue_us, 3),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -129,6 +129,21 @@ pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const 
                          int64_t max_context_len, int32_t path);
 
 /*
+ * pa_decode_profiled -- pa_decode_ex that also times the attention kernel (the
+ * phase-1 kernel of V2, or the V1 kernel): attn_start_event / attn_stop_event
+ * (hipEvent_t created by the caller, or NULL) are recorded by the runtime when
+ * that kernel starts and ends, without adding queue packets between kernels.
+ * workspace == NULL selects the library-owned workspace as in pa_decode.
+ * For measurement harnesses; results are identical to pa_decode_ex.
+ */
+pa_status_t pa_decode_profiled(const pa_dims_t* dims, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int32_t partition_size, void* stream, void* workspace,
+                               size_t workspace_bytes, int64_t max_context_len, int32_t path,
+                               void* attn_start_event, void* attn_stop_event);
+
+/*
  * pa_v2_partition -- V2 phase 1 alone (project_6 commit 96f4baf page,
  * "Phase 1: Per-partition attention").  One work-group per (partition, KV
  * head, sequence) computes, for every query head of the group, the partial

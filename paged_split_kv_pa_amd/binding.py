@@ -50,6 +50,8 @@ SIGNATURES = {
     "pa_workspace_bytes": (_SZ, [_DIMS, _I64, _I32]),
     "pa_decode_ex": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _SZ,
                             _I64, _I32]),
+    "pa_decode_profiled": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
+                                  _SZ, _I64, _I32, _P, _P]),
     "pa_v2_partition": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _I64, _P,
                                _SZ, _P]),
     "pa_v2_reduce": (_I32, [_DIMS, _P, _P, _I32, _I64, _P, _SZ, _P]),
@@ -179,6 +181,19 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale,
     wp, wb = _ws(workspace)
     _check(lib().pa_decode_ex(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
                               _stream(stream), wp, wb, int(max_context_len), int(path)))
+    return out
+
+
+def pa_decode_profiled(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       partition_size=512, stream=None, workspace=None, max_context_len=0,
+                       path=PA_PATH_AUTO, start_event=None, stop_event=None):
+    """pa_decode_ex plus runtime timestamps (hipEvent_t handles) of the attention kernel."""
+    d = dims_of(q, k_cache, block_tables)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    _check(lib().pa_decode_profiled(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
+                                    _stream(stream), wp, wb, int(max_context_len), int(path),
+                                    start_event, stop_event))
     return out
 
 

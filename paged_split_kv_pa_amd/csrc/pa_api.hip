@@ -180,10 +180,11 @@ pa::AttnArgs attn_args(const Plan& pl, void* out, const void* q, const void* k, 
 
 pa_status_t run_partition(const pa_dims_t* dims, const Plan& pl, void* out, const void* q,
                           const void* k, const void* v, const int32_t* bt, const int32_t* ctx,
-                          float scale, void* ws, hipStream_t st) {
+                          float scale, void* ws, hipStream_t st, hipEvent_t e0 = nullptr,
+                          hipEvent_t e1 = nullptr) {
   pa::AttnArgs a = attn_args(pl, out, q, k, v, bt, ctx, scale, ws);
-  return hip_status(pa::launch_attention(dims->dtype, pl.D, pl.G, a, pl.S, st),
-                    "phase-1 attention launch");
+  return hip_status(pa::launch_attention(dims->dtype, pl.D, pl.G, a, pl.S, st, e0, e1),
+                    "attention kernel launch");
 }
 
 pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const int32_t* ctx,
@@ -240,7 +241,7 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
                         const void* v, const int32_t* bt, const int32_t* ctx, float scale,
                         int32_t partition_size, void* stream, void* workspace,
                         size_t workspace_bytes, bool owned, int64_t max_context_len,
-                        int32_t path) {
+                        int32_t path, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   if (path != PA_PATH_AUTO && path != PA_PATH_V1 && path != PA_PATH_V2)
     return fail(PA_ERR_SHAPE, "path %d is not PA_PATH_AUTO, PA_PATH_V1 or PA_PATH_V2", path);
   Plan pl;
@@ -254,7 +255,7 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   if (take == PA_PATH_V1) {
     Plan p1;
     if ((st = make_plan(dims, max_context_len, 0, false, &p1)) != PA_OK) return st;
-    return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs);
+    return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs, e0, e1);
   }
   if (owned) {
     if ((st = owned_workspace(pl.ws_bytes, &workspace)) != PA_OK) return st;
@@ -266,7 +267,8 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
                   workspace_bytes, pl.ws_bytes);
     if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
-  if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs)) != PA_OK)
+  if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs, e0, e1)) !=
+      PA_OK)
     return st;
   return run_reduce(dims, pl, out, ctx, workspace, hs);
 }
@@ -303,6 +305,22 @@ pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const 
     return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                        partition_size, stream, workspace, workspace_bytes, false,
                        max_context_len, path);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_decode_profiled(const pa_dims_t* dims, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int32_t partition_size, void* stream, void* workspace,
+                               size_t workspace_bytes, int64_t max_context_len, int32_t path,
+                               void* attn_start_event, void* attn_stop_event) {
+  try {
+    return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       partition_size, stream, workspace, workspace_bytes, workspace == nullptr,
+                       max_context_len, path, static_cast<hipEvent_t>(attn_start_event),
+                       static_cast<hipEvent_t>(attn_stop_event));
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }

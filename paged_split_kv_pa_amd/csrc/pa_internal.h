@@ -49,8 +49,10 @@ enum class Kernel { kMfma, kValu };
 Kernel kernel_for(int dtype, int group);
 
 // Launch the attention kernel on grid (Pmax, Hkv, S).  Returns the launch status.
+// ev_start / ev_stop (may be null) are recorded when the kernel starts / ends.
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
-                            hipStream_t stream);
+                            hipStream_t stream, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 // Launch the phase-2 kernel on grid (S*Hq, D/32).
 hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
                          hipStream_t stream);

@@ -33,6 +33,8 @@
 // selecting -inf logits and zero V rows (never by multiplying by zero, so
 // stale NaN/Inf in unused cache slots cannot leak into the result).
 
+#include <hip/hip_ext.h>
+
 #include <atomic>
 #include <cstdlib>
 
@@ -61,6 +63,18 @@ constexpr float kLog2e = 1.442695040888963407360f;
 constexpr float kRescaleSlack = 8.f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 raw-buffer format word).
+// A load at an offset >= bytes returns zeros without touching memory, so a
+// resource with bytes = 0 turns every load through it into a no-op.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16-byte streaming load through a buffer resource (non-temporal hint: K/V are
+// read exactly once per step and must not displace reusable cache lines).
+__device__ __forceinline__ u32x4 ld_stream(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
 
 // ---- element conversions -------------------------------------------------------------
 template <int DT>
@@ -209,6 +223,8 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
   const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
 
+  int btv = lane < min(64, kcount) ? btrow[w + NW * lane] : 0;  // first 64 block ids
+
   // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
   // pad the group to 16 heads).  Kept in LDS in lane order: conflict-free 16-byte reads.
   if (w == 0) {
@@ -224,7 +240,6 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   const size_t bstride = (size_t)a.Hkv * hstride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (size_t)g * hstride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + (size_t)g * hstride;
-  __syncthreads();
 
   f32x4 O[NMM];
 #pragma unroll
@@ -234,23 +249,26 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   // kRescaleSlack, so accumulator rescaling is rare; m_max tracks the true max.
   float m_ref = kNegInf, m_max = kNegInf;
   float l_run = 0.f;  // this lane's share of the exp-sum of head r16
-  int btv = 0;        // block ids of the current 64-block chunk, one per lane
 
   u32x4 kbuf[NBUF][NKK], vbuf[NBUF][NC][4];
 
-  auto load_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
-    int phys = __builtin_amdgcn_readlane(btv, kidx);
-    if ((unsigned)phys >= (unsigned)a.NB) phys = 0;
-    const uint16_t* kb = kbase + (size_t)phys * bstride;
-    const uint16_t* vb = vbase + (size_t)phys * bstride;
+  // Loads of one 16-token block (K and V of KV head g).  `real` is false for the
+  // prefetches past the wave's last block: their resources cover 0 bytes, so they
+  // return zeros with no memory traffic while keeping the instruction stream (and
+  // the compiler's wait counts) identical for every stage.  A block id outside the
+  // pool is read the same way, as zeros.
+  auto load_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx, bool real) {
+    const int phys = __builtin_amdgcn_readlane(btv, kidx);
+    const int nbytes = (real && (unsigned)phys < (unsigned)a.NB) ? kBlockSize * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + (size_t)phys * bstride, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + (size_t)phys * bstride, nbytes);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      kr[kk] = *reinterpret_cast<const u32x4*>(kb + r16 * D + 32 * kk + 8 * kg);
+    for (int kk = 0; kk < NKK; ++kk) kr[kk] = ld_stream(rk, (r16 * D + 32 * kk + 8 * kg) * 2);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        vr[c][i] = *reinterpret_cast<const u32x4*>(vb + (4 * kg + i) * D + 128 * c + 8 * r16);
+        vr[c][i] = ld_stream(rv, ((4 * kg + i) * D + 128 * c + 8 * r16) * 2);
   };
 
   auto compute_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
@@ -310,19 +328,37 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
 
   // Blocks are taken 64 at a time (one block id per lane).  Inside a chunk the NBUF
   // register buffers rotate; every stage issues the loads of the block NBUF-1 ahead
-  // (the index is clamped to the chunk's last block, so the loads are unconditional,
-  // the compiler's wait counts stay exact and the prefetch overlaps the compute).
+  // (past the last block those loads are no-ops, see load_block), so the loads are
+  // unconditional, the compiler's wait counts stay exact and the prefetch overlaps
+  // the compute.
+  // The first chunk's block ids were fetched together with the query (one round
+  // trip), and the first chunk's prologue loads are issued before the barrier that
+  // publishes the query: only the first block's math has to wait for it.  Every wave
+  // reaches this barrier exactly once, with or without blocks.
+  // Re-define btv once its load has landed: otherwise the compiler's wait-count
+  // pass keeps treating it as an in-flight load inside the block loop and drains
+  // every outstanding load before each readlane.
+  asm volatile("" : "+v"(btv));
+  if (kcount > 0) {
+    const int last0 = min(64, kcount) - 1;
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) load_block(kbuf[s], vbuf[s], min(s, last0), s <= last0);
+  }
+  __syncthreads();
   for (int c0 = 0; c0 < kcount; c0 += 64) {
     const int cnt = min(64, kcount - c0);
-    btv = lane < cnt ? btrow[w + NW * (c0 + lane)] : 0;
     const int last = cnt - 1;
+    if (c0 > 0) {
+      btv = lane < cnt ? btrow[w + NW * (c0 + lane)] : 0;
+      asm volatile("" : "+v"(btv));
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s) load_block(kbuf[s], vbuf[s], min(s, last));
+      for (int s = 0; s < NBUF - 1; ++s) load_block(kbuf[s], vbuf[s], min(s, last), s <= last);
+    }
     for (int k = 0; k < cnt; k += NBUF) {
 #pragma unroll
       for (int s = 0; s < NBUF; ++s) {
         const int nb = (s + NBUF - 1) % NBUF;
-        load_block(kbuf[nb], vbuf[nb], min(k + s + NBUF - 1, last));
+        load_block(kbuf[nb], vbuf[nb], min(k + s + NBUF - 1, last), k + s + NBUF - 1 <= last);
         // Keep the scheduler from interleaving the next block's loads with this
         // block's math: that would stretch live ranges past the register budget.
         __builtin_amdgcn_sched_barrier(0);
@@ -409,6 +445,17 @@ template <> struct Bytes<4> { typedef uint32_t T; };
 template <> struct Bytes<8> { typedef u32x2 T; };
 template <> struct Bytes<16> { typedef u32x4 T; };
 
+// Streaming load of B (4, 8 or 16) bytes through a buffer resource.
+template <int B>
+__device__ __forceinline__ typename Bytes<B>::T ld_bytes(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (B == 4)
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2);
+  else if constexpr (B == 8)
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+  else
+    return ld_stream(r, off);
+}
+
 // Element e (0-based) of a register run holding elements of type DT.
 template <int DT, typename V>
 __device__ __forceinline__ float elem(const V& v, int e) {
@@ -488,17 +535,16 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   u32x4 kA[KCH], kB[KCH];
   VT vA[16], vB[16];
 
-  auto load_block = [&](u32x4 (&kr)[KCH], VT (&vr)[16], int kidx) {
-    int phys = __builtin_amdgcn_readlane(btv, kidx & 63);
-    if ((unsigned)phys >= (unsigned)a.NB) phys = 0;
-    const unsigned char* kb = kbase + (size_t)phys * bstride;
-    const unsigned char* vb = vbase + (size_t)phys * bstride;
+  // Same loading scheme as attn_mfma_kernel: buffer loads, no-op past the last block.
+  auto load_block = [&](u32x4 (&kr)[KCH], VT (&vr)[16], int kidx, bool real) {
+    const int phys = __builtin_amdgcn_readlane(btv, kidx);
+    const int nbytes = (real && (unsigned)phys < (unsigned)a.NB) ? kBlockSize * ROWB : 0;
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + (size_t)phys * bstride, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + (size_t)phys * bstride, nbytes);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      kr[j] = *reinterpret_cast<const u32x4*>(kb + t * ROWB + (r + 4 * j) * 16);
+    for (int j = 0; j < KCH; ++j) kr[j] = ld_stream(rk, t * ROWB + (r + 4 * j) * 16);
 #pragma unroll
-    for (int t2 = 0; t2 < 16; ++t2)
-      vr[t2] = *reinterpret_cast<const VT*>(vb + t2 * ROWB + lane * VB);
+    for (int t2 = 0; t2 < 16; ++t2) vr[t2] = ld_bytes<VB>(rv, t2 * ROWB + lane * VB);
   };
 
   auto compute_block = [&](u32x4 (&kr)[KCH], VT (&vr)[16], int kidx) {
@@ -582,13 +628,14 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   for (int c0 = 0; c0 < kcount; c0 += 64) {
     const int cnt = min(64, kcount - c0);
     btv = lane < cnt ? btrow[w + kWaves * (c0 + lane)] : 0;
+    asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
     const int last = cnt - 1;
-    load_block(kA, vA, 0);
+    load_block(kA, vA, 0, true);
     for (int k = 0; k < cnt; k += 2) {
-      load_block(kB, vB, min(k + 1, last));
+      load_block(kB, vB, min(k + 1, last), k + 1 <= last);
       compute_block(kA, vA, c0 + k);
       if (k + 1 >= cnt) break;
-      load_block(kA, vA, min(k + 2, last));
+      load_block(kA, vA, min(k + 2, last), k + 2 <= last);
       compute_block(kB, vB, c0 + k + 1);
     }
   }
@@ -661,25 +708,19 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
 // Phase 2: cross-partition log-sum-exp merge.
 // Grid (S*Hq, D/32); 256 threads = 32 partition lanes x 8 float4 columns.
 // =======================================================================================
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s);
-  return v;
-}
-
 template <int DT, int D>
 __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
-  extern __shared__ float s_w[];  // [Pmax] rescaled exp-sums r_p
-  __shared__ float s_red[4];
+  // Thread (pg, d4): partition lane pg (32 of them) and 4 of the 32 columns of this
+  // work-group.  Each thread folds its partitions pg, pg+32, ... with the running
+  // log-sum-exp rule; the partitions' loads do not depend on each other, so the
+  // whole partial set is requested in one memory round trip.  The 32 lanes are then
+  // folded in a fixed order (bitwise deterministic).
+  __shared__ float s_m[32], s_s[32];
   __shared__ f32x4 s_acc[32][8];
   const int bh = blockIdx.x, chunk = blockIdx.y;
   const int b = bh / a.Hq;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int d4 = tid & 7, pg = tid >> 3;
 
   int n = a.ctx[b];
   const int cap = a.MB * kBlockSize;
@@ -689,36 +730,40 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   if (nparts <= 1) return;  // phase 1 wrote the final output (or zeros)
 
   const size_t base = (size_t)bh * a.Pmax;
-  float mx = kNegInf;
-  for (int q = tid; q < nparts; q += 256) mx = fmaxf(mx, a.max_logits[base + q]);
-  mx = wave_max(mx);
-  if (lane == 0) s_red[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-  float sum = 0.f;
-  for (int q = tid; q < nparts; q += 256) {
-    const float rq = exp2_fast((a.max_logits[base + q] - M) * kLog2e) * a.exp_sums[base + q];
-    s_w[q] = rq;
-    sum += rq;
-  }
-  sum = wave_sum(sum);
-  if (lane == 0) s_red[w] = sum;
-  __syncthreads();
-  const float inv = 1.f / ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
-
-  const int d4 = tid & 7, pg = tid >> 3;
   const float* src = a.tmp_out + base * D + chunk * 32 + d4 * 4;
+  float M = kNegInf, S = 0.f;  // base-2 running max and exp-sum of this thread's partitions
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int q = pg; q < nparts; q += 32)
-    acc += s_w[q] * *reinterpret_cast<const f32x4*>(src + (size_t)q * D);
+#pragma unroll 8
+  for (int q = pg; q < nparts; q += 32) {
+    const float mq = a.max_logits[base + q] * kLog2e;
+    const float sq = a.exp_sums[base + q];
+    const f32x4 oq = *reinterpret_cast<const f32x4*>(src + (size_t)q * D);
+    const float Mn = fmaxf(M, mq);
+    const float c_old = exp2_fast(M - Mn);   // 0 when M is -inf
+    const float c_new = exp2_fast(mq - Mn) * sq;
+    S = S * c_old + c_new;
+    acc = acc * c_old + oq * c_new;
+    M = Mn;
+  }
+  if (d4 == 0) {
+    s_m[pg] = M;
+    s_s[pg] = S;
+  }
   s_acc[pg][d4] = acc;
   __syncthreads();
   if (tid < 8) {
+    float Mt = s_m[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) Mt = fmaxf(Mt, s_m[i]);
+    float St = 0.f;
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 32; ++q) tot += s_acc[q][tid];
+    for (int i = 0; i < 32; ++i) {
+      const float c = s_m[i] == kNegInf ? 0.f : exp2_fast(s_m[i] - Mt);
+      St += c * s_s[i];
+      tot += c * s_acc[i][tid];
+    }
+    const float inv = 1.f / St;
     const float vals[4] = {tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
     store_out<DT, 4>(a.out, (size_t)bh * D + chunk * 32 + tid * 4, vals);
   }
@@ -742,58 +787,59 @@ int mfma_variant() {
   return v;
 }
 
+struct Launch {
+  dim3 grid;
+  hipStream_t st;
+  hipEvent_t e0, e1;
+};
+
+template <typename K>
+void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
+  hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a);
+}
+
 template <int DT, int D, int G>
-hipError_t launch_attn_t(const AttnArgs& a, int S, hipStream_t st) {
-  dim3 grid(a.Pmax, a.Hkv, S);
+hipError_t launch_attn_t(const AttnArgs& a, const Launch& l) {
   if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
     switch (mfma_variant()) {
-      case 0:
-        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>), grid,
-                           dim3(2 * 64), 0, st, a);
-        break;
-      case 1:
-        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>), grid,
-                           dim3(64), 0, st, a);
-        break;
-      default:
-        hipLaunchKernelGGL((attn_mfma_kernel<DT, D, G, 4, 2>), grid, dim3(4 * 64), 0, st, a);
-        break;
+      case 0: launch(attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>, l, 2 * 64, a); break;
+      case 1: launch(attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>, l, 64, a); break;
+      default: launch(attn_mfma_kernel<DT, D, G, 4, 2>, l, 4 * 64, a); break;
     }
   } else {
-    hipLaunchKernelGGL((attn_valu_kernel<DT, D, G>), grid, dim3(kThreads), 0, st, a);
+    launch(attn_valu_kernel<DT, D, G>, l, kThreads, a);
   }
   return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t launch_attn_g(int G, const AttnArgs& a, int S, hipStream_t st) {
+hipError_t launch_attn_g(int G, const AttnArgs& a, const Launch& l) {
   switch (G) {
-    case 1: return launch_attn_t<DT, D, 1>(a, S, st);
-    case 2: return launch_attn_t<DT, D, 2>(a, S, st);
-    case 4: return launch_attn_t<DT, D, 4>(a, S, st);
-    case 8: return launch_attn_t<DT, D, 8>(a, S, st);
-    case 16: return launch_attn_t<DT, D, 16>(a, S, st);
+    case 1: return launch_attn_t<DT, D, 1>(a, l);
+    case 2: return launch_attn_t<DT, D, 2>(a, l);
+    case 4: return launch_attn_t<DT, D, 4>(a, l);
+    case 8: return launch_attn_t<DT, D, 8>(a, l);
+    case 16: return launch_attn_t<DT, D, 16>(a, l);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
-hipError_t launch_attn_d(int D, int G, const AttnArgs& a, int S, hipStream_t st) {
-  if (D == 128) return launch_attn_g<DT, 128>(G, a, S, st);
-  if (D == 256) return launch_attn_g<DT, 256>(G, a, S, st);
+hipError_t launch_attn_d(int D, int G, const AttnArgs& a, const Launch& l) {
+  if (D == 128) return launch_attn_g<DT, 128>(G, a, l);
+  if (D == 256) return launch_attn_g<DT, 256>(G, a, l);
   return hipErrorInvalidValue;
 }
 
 template <int DT>
 hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
   dim3 block(256);
-  const size_t shmem = (size_t)a.Pmax * sizeof(float);
   if (D == 128) {
     dim3 grid((unsigned)(S * a.Hq), 128 / 32);
-    hipLaunchKernelGGL((reduce_kernel<DT, 128>), grid, block, shmem, st, a);
+    hipLaunchKernelGGL((reduce_kernel<DT, 128>), grid, block, 0, st, a);
   } else if (D == 256) {
     dim3 grid((unsigned)(S * a.Hq), 256 / 32);
-    hipLaunchKernelGGL((reduce_kernel<DT, 256>), grid, block, shmem, st, a);
+    hipLaunchKernelGGL((reduce_kernel<DT, 256>), grid, block, 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -815,11 +861,12 @@ Kernel kernel_for(int dtype, int group) {
 }
 
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const Launch l{dim3(a.Pmax, a.Hkv, num_seqs), stream, ev_start, ev_stop};
   switch (dtype) {
-    case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, a, num_seqs, stream);
-    case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, a, num_seqs, stream);
-    case PA_BF16: return launch_attn_d<PA_BF16>(head_dim, group, a, num_seqs, stream);
+    case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, a, l);
+    case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, a, l);
+    case PA_BF16: return launch_attn_d<PA_BF16>(head_dim, group, a, l);
     default: return hipErrorInvalidValue;
   }
 }
