@@ -106,10 +106,18 @@ pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const voi
  *   tmp_out     [S, Hq, Pmax, D]  normalised partial output of each partition
  *   max_logits  [S, Hq, Pmax]     max over the partition of scale*q.k
  *   exp_sums    [S, Hq, Pmax]     sum over the partition of exp(logit - max)
- * Returns 0 when the arguments are invalid (see pa_last_error()).
+ * pa_workspace_layout() returns the offsets.  The contents need no
+ * initialisation.  Returns 0 when the arguments are invalid (see pa_last_error()).
  */
 size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
                           int32_t partition_size);
+
+/* Workspace layout for these arguments, written to layout[0..PA_LAYOUT_FIELDS-1]:
+ * Pmax, then the byte offsets of tmp_out, max_logits and exp_sums, then the
+ * total bytes. */
+#define PA_LAYOUT_FIELDS 5
+pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
+                                int32_t partition_size, int64_t* layout);
 
 /*
  * pa_decode_ex -- pa_decode with caller-chosen path, context bound and
@@ -119,8 +127,9 @@ size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
  * It must not exceed MB*16; tokens beyond it are not attended.
  * workspace: device memory of >= pa_workspace_bytes(dims, max_context_len,
  * partition_size) bytes, needed only when the path taken is V2 (may be NULL
- * for V1).  Its contents after the call are the phase-1 partials (layout
- * above) for sequences with more than one partition.
+ * for V1).  V2 enqueues two launches, phase 1 then phase 2; after the call the
+ * workspace holds the phase-1 partials (layout above) of every sequence with
+ * more than one partition.  Calls that overlap on the same workspace race.
  */
 pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_tables,
@@ -144,7 +153,7 @@ pa_status_t pa_decode_profiled(const pa_dims_t* dims, void* out, const void* q,
                                void* attn_start_event, void* attn_stop_event);
 
 /*
- * pa_v2_partition -- V2 phase 1 alone (project_6 commit 96f4baf page,
+ * pa_v2_partition -- V2 phase 1 as its own launch (project_6 commit 96f4baf page,
  * "Phase 1: Per-partition attention").  One work-group per (partition, KV
  * head, sequence) computes, for every query head of the group, the partial
  * output, exp-sum and max logit of its partition and writes them to the
@@ -159,7 +168,7 @@ pa_status_t pa_v2_partition(const pa_dims_t* dims, void* out, const void* q,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_v2_reduce -- V2 phase 2 alone (project_6 commit 96f4baf page, "Phase 2:
+ * pa_v2_reduce -- V2 phase 2 as its own launch (project_6 commit 96f4baf page, "Phase 2:
  * Cross-partition reduction (log-sum-exp)").  For each (sequence, query
  * head) with more than one partition: M = max_p max_logits[p],
  * r_p = exp(max_logits[p] - M) * exp_sums[p], out = sum_p r_p tmp_out[p] /

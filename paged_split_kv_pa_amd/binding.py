@@ -48,6 +48,7 @@ _DIMS = ctypes.POINTER(PaDims)
 SIGNATURES = {
     "pa_decode": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P]),
     "pa_workspace_bytes": (_SZ, [_DIMS, _I64, _I32]),
+    "pa_workspace_layout": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
     "pa_decode_ex": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _SZ,
                             _I64, _I32]),
     "pa_decode_profiled": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P,
@@ -269,19 +270,17 @@ def pa_get_mfma_variant():
 
 
 def workspace_layout(q, k_cache, block_tables, max_context_len=0, partition_size=512):
-    """Views into a V2 workspace: offsets and shapes of tmp_out / max_logits / exp_sums.
+    """Section offsets of a V2 workspace, as the library computes them.
 
-    Mirrors the layout documented for pa_workspace_bytes (fp32 sections, each
-    starting on a 256-byte boundary).
+    Returns a dict: pmax, bytes, and for tmp_out / max_logits / exp_sums a
+    (byte offset, shape) pair; all three are fp32, tmp_out [S, Hq, pmax, D] and
+    the statistics [S, Hq, pmax].
     """
-    S, Hq, D = q.shape
-    cap = block_tables.shape[1] * k_cache.shape[2]
-    bound = max_context_len if max_context_len > 0 else cap
-    pmax = -(-bound // partition_size)
-    rows = S * Hq * pmax
-    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    off_max = a256(rows * D * 4)
-    off_sum = off_max + a256(rows * 4)
-    return {"pmax": pmax, "tmp_out": (0, (S, Hq, pmax, D)),
-            "max_logits": (off_max, (S, Hq, pmax)), "exp_sums": (off_sum, (S, Hq, pmax)),
-            "bytes": off_sum + a256(rows * 4)}
+    d = dims_of(q, k_cache, block_tables)
+    v = (ctypes.c_int64 * 5)()
+    _check(lib().pa_workspace_layout(ctypes.byref(d), int(max_context_len),
+                                     int(partition_size), v))
+    pmax, o_tmp, o_max, o_sum, nbytes = list(v)
+    S, Hq, D = d.num_seqs, d.num_q_heads, d.head_dim
+    return {"pmax": pmax, "bytes": nbytes, "tmp_out": (o_tmp, (S, Hq, pmax, D)),
+            "max_logits": (o_max, (S, Hq, pmax)), "exp_sums": (o_sum, (S, Hq, pmax))}

@@ -57,7 +57,8 @@ struct Plan {
   int64_t ctx_bound;  // planning bound on every context length
   int32_t P;          // partition size used by the kernels
   int64_t Pmax;       // partition-grid size
-  size_t off_tmp, off_max, off_sum, ws_bytes;
+  size_t off_tmp, off_max, off_sum;  // phase-1 partials
+  size_t ws_bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -294,6 +295,18 @@ size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
   Plan pl;
   if (make_plan(dims, max_context_len, partition_size, true, &pl) != PA_OK) return 0;
   return pl.ws_bytes;
+}
+
+pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
+                                int32_t partition_size, int64_t* layout) {
+  if (!layout) return fail(PA_ERR_NULL, "layout is NULL");
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  const int64_t v[PA_LAYOUT_FIELDS] = {pl.Pmax, (int64_t)pl.off_tmp, (int64_t)pl.off_max,
+                                       (int64_t)pl.off_sum, (int64_t)pl.ws_bytes};
+  for (int i = 0; i < PA_LAYOUT_FIELDS; ++i) layout[i] = v[i];
+  return ok();
 }
 
 pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,

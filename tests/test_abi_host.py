@@ -110,19 +110,34 @@ def test_empty_batch_is_a_no_op():
     assert decode(dims(num_seqs=0), nul) == 0
 
 
+def layout(d, hint, P):
+    v = (ctypes.c_int64 * 5)()
+    assert B.lib().pa_workspace_layout(ctypes.byref(d), hint, P, v) == 0
+    return list(v)
+
+
 def test_workspace_bytes_layout():
     d = dims(num_seqs=3, max_blocks_per_seq=100)  # capacity 1600 tokens
-    n = B.lib().pa_workspace_bytes(ctypes.byref(d), 0, 512)
-    pmax = 4  # ceil(1600 / 512)
-    rows = 3 * 32 * pmax
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert n == a256(rows * 128 * 4) + 2 * a256(rows * 4)
-    # A context hint shrinks the partition grid.
-    n2 = B.lib().pa_workspace_bytes(ctypes.byref(d), 513, 512)
-    assert n2 == a256(3 * 32 * 2 * 128 * 4) + 2 * a256(3 * 32 * 2 * 4)
-    # Invalid: hint above capacity, bad partition size.
+    for hint, P, pmax in ((0, 512, 4), (513, 512, 2), (0, 16, 100)):
+        rows = 3 * 32 * pmax
+        off_max = a256(rows * 128 * 4)
+        off_sum = off_max + a256(rows * 4)
+        total = off_sum + a256(rows * 4)
+        assert layout(d, hint, P) == [pmax, 0, off_max, off_sum, total]
+        assert B.lib().pa_workspace_bytes(ctypes.byref(d), hint, P) == total
+    # Invalid: hint above capacity, bad partition size, NULL output.
     assert B.lib().pa_workspace_bytes(ctypes.byref(d), 1601, 512) == 0
     assert B.lib().pa_workspace_bytes(ctypes.byref(d), 0, 24) == 0
+    v = (ctypes.c_int64 * 5)()
+    assert B.lib().pa_workspace_layout(ctypes.byref(d), 0, 24, v) == -5
+    assert B.lib().pa_workspace_layout(ctypes.byref(d), 0, 512, None) == -1
+
+
+def test_long_context_partition_grid():
+    # 100000 tokens at P = 512: 196 partitions (tests/golden/partition_counts.txt).
+    d = dims(num_seqs=1, max_blocks_per_seq=6250)
+    assert layout(d, 0, 512)[0] == 196
 
 
 def test_workspace_required_for_v2():

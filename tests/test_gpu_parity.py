@@ -52,7 +52,7 @@ def run_path(w, dev, path, P, variant=None, max_context_len=0):
     if path != B.PA_PATH_V1:
         nbytes = B.pa_workspace_bytes(dev["q"], dev["k_cache"], dev["block_tables"],
                                       max_context_len, P)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     if variant is not None:
         B.pa_set_mfma_variant(variant)
     B.pa_decode_ex(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
@@ -246,11 +246,14 @@ def test_runs_are_bitwise_deterministic(cfg):
 
 
 def test_pa_decode_equals_its_two_phases():
+    """pa_decode (library workspace) == pa_decode_ex V2 == pa_v2_partition + pa_v2_reduce,
+    bit for bit, and within tolerance of the oracle."""
     w, dev, ref = config_case(2)
-    say("pa_decode vs phases on long_100k")
+    say("pa_decode vs pa_decode_ex vs the two phases on long_100k")
     out1 = torch.empty_like(dev["q"])
     B.pa_decode(out1, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                 dev["context_lens"], w.scale, 512)
+    out0 = run_path(w, dev, B.PA_PATH_V2, 512)
     lay = B.workspace_layout(dev["q"], dev["k_cache"], dev["block_tables"], 0, 512)
     ws = torch.empty(lay["bytes"], dtype=torch.uint8, device="cuda")
     out2 = torch.empty_like(dev["q"])
@@ -259,8 +262,31 @@ def test_pa_decode_equals_its_two_phases():
     B.pa_v2_reduce(out2, dev["q"], dev["k_cache"], dev["block_tables"], dev["context_lens"], ws,
                    512)
     torch.cuda.synchronize()
+    assert torch.equal(out1, out0)
     assert torch.equal(out1, out2)
     check_close(to_f64(out1), ref, "pa_decode long_100k")
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, consecutive calls whose partition counts differ per sequence."""
+    P = 64
+    big = small_workload(41, [3000, 640, 65, 1, 0, 2000], Hq=16, Hkv=2, D=128, dtype="bf16",
+                         max_blocks_per_seq=200)
+    dev = upload(big)
+    lay = B.workspace_layout(dev["q"], dev["k_cache"], dev["block_tables"], 0, P)
+    ws = torch.empty(lay["bytes"], dtype=torch.uint8, device="cuda")
+    for step, lens in enumerate(([3000, 640, 65, 1, 0, 2000], [100, 3199, 64, 700, 5, 1],
+                                 [3200, 3200, 3200, 3200, 3200, 3200], [0, 0, 1, 0, 0, 17])):
+        say(f"workspace reuse step {step} lens={lens}")
+        ctx = np.array(lens, dtype=np.int32)
+        ref = oracle.decode_attention(big.q, big.k_cache, big.v_cache, big.block_tables, ctx,
+                                      big.scale, big.dtype)
+        out = torch.empty_like(dev["q"])
+        B.pa_decode_ex(out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                       torch.from_numpy(ctx).cuda(), big.scale, P, workspace=ws,
+                       path=B.PA_PATH_V2)
+        torch.cuda.synchronize()
+        check_close(to_f64(out), ref, f"reuse step {step}")
 
 
 def test_context_hint_and_side_stream():
@@ -274,3 +300,4 @@ def test_context_hint_and_side_stream():
     check_close(to_f64(out), ref, "hinted")
     full = run_path(w, dev, B.PA_PATH_V2, 512)
     assert torch.equal(out, full)
+
