@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = 100K context)")
     ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--path", choices=("auto", "v1", "v2"), default="auto",
+                    help="decode path (auto = the library's rule)")
     ap.add_argument("--copies", type=int, default=0,
                     help="KV pool replicas rotated across steps (0 = enough for >= 1 GiB)")
     ap.add_argument("--variant", type=int, default=-1, help="matrix-core kernel variant")
@@ -69,6 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--sweep-paths", action="store_true",
+                    help="time forced V1 against forced V2 over a grid of batch sizes and "
+                         "context lengths (32/4 heads, head_dim 128, bf16) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference "
                          "kernel for scaling hardware byte counters), then exit")
@@ -124,6 +129,52 @@ def cpu_baseline(w, seconds):
                       f"gather + upcast + softmax attention), {el:.1f} s wall"}, ref
 
 
+def sweep_paths(steps=40, warmup=5):
+    """Forced V1 vs forced V2 step time over (batch, context); prints JSON lines.
+
+    Inputs are random bf16 tensors drawn on the device (the values do not matter for
+    timing; parity is covered by the tests).  Steps run back to back on one pool, so
+    small cases are cache-warm; both paths see the same conditions.
+    """
+    import torch
+    from paged_split_kv_pa_amd import binding as B
+    Hq, Hkv, D, P = 32, 4, 128, 512
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    rows = []
+    for S in (1, 4, 16, 64, 256):
+        for n in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+            if S * n > (1 << 20):
+                continue
+            nb = -(-n // 16)
+            NB = S * nb + 1
+            q = torch.randn(S, Hq, D, device="cuda", dtype=torch.bfloat16, generator=gen)
+            k = torch.randn(NB, Hkv, 16, D, device="cuda", dtype=torch.bfloat16, generator=gen)
+            v = torch.randn_like(k)
+            bt = torch.randperm(NB - 1, device="cuda", generator=gen)[:S * nb].view(S, nb)
+            bt = bt.to(torch.int32).contiguous()
+            ctx = torch.full((S,), n, dtype=torch.int32, device="cuda")
+            out = torch.empty_like(q)
+            ws = torch.empty(B.pa_workspace_bytes(q, k, bt, 0, P), dtype=torch.uint8,
+                             device="cuda")
+            res = {}
+            for name, path in (("v1", B.PA_PATH_V1), ("v2", B.PA_PATH_V2)):
+                for _ in range(warmup):
+                    B.pa_decode_ex(out, q, k, v, bt, ctx, 0.088, P, workspace=ws, path=path)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    B.pa_decode_ex(out, q, k, v, bt, ctx, 0.088, P, workspace=ws, path=path)
+                torch.cuda.synchronize()
+                res[name] = (time.perf_counter() - t0) * 1e6 / steps
+            rec = {"num_seqs": S, "context": n, "us_v1": round(res["v1"], 2),
+                   "us_v2": round(res["v2"], 2),
+                   "faster": "v1" if res["v1"] <= res["v2"] else "v2"}
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+            del q, k, v, bt, ctx, out, ws
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -134,6 +185,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sweep_paths:
+        sweep_paths()
         return
 
     from paged_split_kv_pa_amd import binding as B
@@ -160,7 +214,8 @@ def main():
     ctx = torch.from_numpy(w.context_lens).cuda()
     out = torch.empty_like(q)
     ws = torch.zeros(B.pa_workspace_bytes(q, kc0, bt, 0, P), dtype=torch.uint8, device="cuda")
-    path = B.pa_choose_path(B.dims_of(q, kc0, bt))
+    path = {"auto": B.pa_choose_path(B.dims_of(q, kc0, bt), 0, P), "v1": B.PA_PATH_V1,
+            "v2": B.PA_PATH_V2}[args.path]
     stream = torch.cuda.current_stream()
 
     # Argument tuples are marshalled once, so a step costs two plain C calls on the
@@ -234,6 +289,9 @@ def main():
         f"kernel mean {k1_mean:.2f} us (median {np.median(k1):.2f}, p10 "
         f"{np.percentile(k1, 10):.2f}, p90 {np.percentile(k1, 90):.2f})")
 
+    mfma = w.dtype != "f32" and w.num_q_heads // w.num_kv_heads >= 4
+    kernel_name = ("attn_mfma_kernel" if mfma else "attn_valu_kernel") + \
+        (" (V1 single pass)" if path == B.PA_PATH_V1 else " (V2 phase 1)")
     value = kvb / (ms_per_step / 1e3) / 1e9
     achieved = kvb / (k1_mean / 1e6) / 1e9
     rec = {
@@ -264,7 +322,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic() if args.config == 2 and P == 512 else None,
-            "kernel": "attn_mfma_kernel (phase 1)", "kernel_mean_us": round(k1_mean, 3),
+            "kernel": kernel_name, "kernel_mean_us": round(k1_mean, 3),
             "kernel_samples": len(k1),
         },
         "host_enqueue_us_per_step": round(enqueue_us, 3),

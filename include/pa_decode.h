@@ -15,7 +15,9 @@
  *     "_PARTITION_SIZE inconsistency": both phases must use one partition size.
  *     Here it is a single run-time argument, so they cannot disagree.
  *   - project_6 commit a2a5dd8 ("computility-run.yaml" commit page), decode
- *     path summary: V1 for contexts up to 8192 tokens, V2 above.
+ *     path summary: V1 for contexts up to 8192 tokens, V2 above (available as
+ *     a setting; the default rule is the one measured on MI355X, see
+ *     pa_set_v1_max_context).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -86,9 +88,9 @@ typedef struct pa_dims {
 
 /*
  * pa_decode -- one decode step, path chosen by context length.
- * The context bound used for planning is MB*16 (the block-table capacity); it
- * picks V1 when it is <= the V1 threshold (pa_set_v1_max_context), else V2
- * with partitions of partition_size tokens.  V2 uses a library-owned
+ * The context bound used for planning is MB*16 (the block-table capacity); the
+ * path follows pa_set_v1_max_context's rule (V1, or V2 with partitions of
+ * partition_size tokens).  V2 uses a library-owned
  * workspace that grows on demand (hipMalloc on the first call that needs
  * more) and is kept per device; calls that overlap on one device from
  * different streams must use pa_decode_ex with their own workspaces.
@@ -121,7 +123,7 @@ pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
 
 /*
  * pa_decode_ex -- pa_decode with caller-chosen path, context bound and
- * workspace.  path: PA_PATH_AUTO, PA_PATH_V1 or PA_PATH_V2.
+ * workspace.  path: PA_PATH_AUTO (pa_choose_path's rule), PA_PATH_V1 or PA_PATH_V2.
  * max_context_len: upper bound on every context_lens[b] (<= 0: MB*16); it
  * sizes the partition grid, so a smaller bound means fewer idle work-groups.
  * It must not exceed MB*16; tokens beyond it are not attended.
@@ -190,14 +192,18 @@ pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k
                   const int32_t* context_lens, float scale, int64_t max_context_len,
                   void* stream);
 
-/* Path pa_decode would take for this context bound (<= 0: MB*16):
- * PA_PATH_V1 or PA_PATH_V2, or a negative pa_status_t for invalid dims. */
-int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len);
+/* Path pa_decode / PA_PATH_AUTO would take for this context bound (<= 0:
+ * MB*16) and partition size: PA_PATH_V1 or PA_PATH_V2, or a negative
+ * pa_status_t for invalid dims. */
+int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size);
 
-/* V1 threshold in tokens (V1 when the context bound is <= it).  Default 8192
- * (project_6 commit a2a5dd8 page, decode path summary), or the value of the
- * environment variable PA_V1_MAX_CONTEXT read at library load.  0 disables V1
- * in the automatic choice.  Process-wide; safe to call from any thread. */
+/* V1/V2 rule.  tokens >= 0: the pages' context-length rule, V1 iff the context
+ * bound <= tokens (project_6 commit a2a5dd8 page, decode paths: 8192); 0 means
+ * never V1.  tokens < 0 (the default): the rule measured on MI355X -- V1 iff the
+ * bound fits in one partition, or S*Hkv >= 256 so that the one-work-group-per-
+ * (sequence, KV head) V1 grid already fills the 256 compute units; V2 otherwise.
+ * The environment variable PA_V1_MAX_CONTEXT sets the initial value.  The getter
+ * returns -1 for the measured rule.  Process-wide; safe from any thread. */
 void pa_set_v1_max_context(int64_t tokens);
 int64_t pa_get_v1_max_context(void);
 
@@ -216,9 +222,10 @@ const char* pa_version(void);
 
 /* Tuning knob for the fp16/bf16 kernel with G >= 4: work-group shape
  *   0 = 2 waves per (partition, KV head, sequence), 3-deep (D=128) / 2-deep
- *       (D=256) register pipeline per wave  [default]
+ *       (D=256) register pipeline per wave
  *   1 = 1 wave, 5-deep / 3-deep pipeline
  *   2 = 4 waves, 2-deep pipeline
+ *  -1 = automatic (the default): 1 for grids of >= 512 work-groups, else 0.
  * All variants compute the same result (to rounding).  The environment
  * variable PA_MFMA_VARIANT sets the initial value.  Process-wide; do not
  * change it while another thread is launching.  Returns PA_ERR_UNSUPPORTED

@@ -57,7 +57,7 @@ SIGNATURES = {
                                _SZ, _P]),
     "pa_v2_reduce": (_I32, [_DIMS, _P, _P, _I32, _I64, _P, _SZ, _P]),
     "pa_v1": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _P]),
-    "pa_choose_path": (_I32, [_DIMS, _I64]),
+    "pa_choose_path": (_I32, [_DIMS, _I64, _I32]),
     "pa_set_v1_max_context": (None, [_I64]),
     "pa_get_v1_max_context": (_I64, []),
     "pa_num_partitions": (_I64, [_I64, _I32]),
@@ -229,8 +229,8 @@ def pa_v1(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_conte
     return out
 
 
-def pa_choose_path(dims, max_context_len=0):
-    r = lib().pa_choose_path(ctypes.byref(dims), int(max_context_len))
+def pa_choose_path(dims, max_context_len=0, partition_size=512):
+    r = lib().pa_choose_path(ctypes.byref(dims), int(max_context_len), int(partition_size))
     if r < 0:
         raise PaError(r, pa_last_error())
     return r

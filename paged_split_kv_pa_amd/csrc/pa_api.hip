@@ -22,15 +22,23 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// V1/V2 choice.  A value >= 0 is a context-length threshold (V1 iff the planning
+// bound is <= it: the rule of project_6 commit a2a5dd8 page, decode paths, where it is
+// 8192).  The default -1 selects the rule measured on MI355X: V1 iff the bound fits
+// one partition, or the V1 grid (one work-group per sequence and KV head) alone
+// already fills the device; otherwise V2.
+constexpr int64_t kMeasuredRule = -1;
+constexpr int64_t kV1FillWorkgroups = 256;  // MI355X compute units
+
 std::atomic<int64_t>& v1_threshold() {
   static std::atomic<int64_t> t([] {
     const char* env = std::getenv("PA_V1_MAX_CONTEXT");
     if (env && *env) {
       char* end = nullptr;
       long long v = std::strtoll(env, &end, 10);
-      if (end && *end == '\0' && v >= 0) return (int64_t)v;
+      if (end && *end == '\0' && v >= kMeasuredRule) return (int64_t)v;
     }
-    return (int64_t)8192;  // V1 up to 8192 tokens: project_6 commit a2a5dd8 page, decode paths
+    return kMeasuredRule;
   }());
   return t;
 }
@@ -233,9 +241,12 @@ pa_status_t owned_workspace(size_t bytes, void** out) {
   return ok();
 }
 
-int32_t choose(const Plan& pl) {
+int32_t choose(const Plan& pl, int32_t partition_size) {
   const int64_t t = v1_threshold().load();
-  return pl.ctx_bound <= t ? PA_PATH_V1 : PA_PATH_V2;
+  if (t >= 0) return pl.ctx_bound <= t ? PA_PATH_V1 : PA_PATH_V2;
+  const bool one_partition = partition_size > 0 && pl.ctx_bound <= partition_size;
+  const bool v1_fills = (int64_t)pl.S * pl.Hkv >= kV1FillWorkgroups;
+  return (one_partition || v1_fills) ? PA_PATH_V1 : PA_PATH_V2;
 }
 
 pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const void* k,
@@ -251,7 +262,7 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   if (pl.S == 0) return ok();
   if ((st = check_tensors(out, q, k, v, bt, ctx)) != PA_OK) return st;
   if ((st = check_scale(scale)) != PA_OK) return st;
-  const int32_t take = path == PA_PATH_AUTO ? choose(pl) : path;
+  const int32_t take = path == PA_PATH_AUTO ? choose(pl, partition_size) : path;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (take == PA_PATH_V1) {
     Plan p1;
@@ -391,14 +402,16 @@ pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k
                        nullptr, static_cast<hipStream_t>(stream));
 }
 
-int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len) {
+int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size) {
   Plan pl;
   pa_status_t st = make_plan(dims, max_context_len, 0, false, &pl);
   if (st != PA_OK) return st;
-  return choose(pl);
+  return choose(pl, partition_size);
 }
 
-void pa_set_v1_max_context(int64_t tokens) { v1_threshold().store(tokens < 0 ? 0 : tokens); }
+void pa_set_v1_max_context(int64_t tokens) {
+  v1_threshold().store(tokens < 0 ? kMeasuredRule : tokens);
+}
 
 int64_t pa_get_v1_max_context(void) { return v1_threshold().load(); }
 
@@ -426,7 +439,7 @@ const char* pa_version(void) { return "pa_decode 0.1.0 gfx950"; }
 
 pa_status_t pa_set_mfma_variant(int32_t variant) {
   if (pa::set_mfma_variant(variant) != 0)
-    return fail(PA_ERR_UNSUPPORTED, "matrix-core variant %d unknown (0, 1 or 2)", variant);
+    return fail(PA_ERR_UNSUPPORTED, "matrix-core variant %d unknown (-1, 0, 1 or 2)", variant);
   return ok();
 }
 

@@ -39,8 +39,8 @@ struct ReduceArgs {
   int32_t Hq, MB, P, Pmax;
 };
 
-// Work-group shape of the matrix-core kernel (0, 1 or 2; see pa_kernels.hip).
-// set_mfma_variant returns -1 for an unknown variant.
+// Work-group shape of the matrix-core kernel (-1 automatic, 0, 1 or 2; see
+// pa_kernels.hip).  set_mfma_variant returns -1 for an unknown variant.
 int set_mfma_variant(int v);
 int get_mfma_variant();
 

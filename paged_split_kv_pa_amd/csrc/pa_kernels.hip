@@ -771,20 +771,32 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
 
 // ---- dispatch --------------------------------------------------------------------------
 // Work-group shape of the matrix-core kernel (see attn_mfma_kernel):
-//   0 = 2 waves, pipeline depth 3 (head_dim 128) / 2 (head_dim 256)  [default]
+//   0 = 2 waves, pipeline depth 3 (head_dim 128) / 2 (head_dim 256)
 //   1 = 1 wave,  pipeline depth 5 / 3
 //   2 = 4 waves, pipeline depth 2
-std::atomic<int> g_mfma_variant{-1};
+//  -1 = automatic (default): 1 when the grid has at least two work-groups per
+//       compute unit (the long-context shape streams best with one wave per
+//       work-group), else 0 (more waves for small grids).
+constexpr int kAutoVariant = -1;
+constexpr long long kAutoOneWaveGrid = 512;
+std::atomic<int> g_mfma_variant{-2};  // -2: not yet read from the environment
 
-int mfma_variant() {
+int mfma_variant_setting() {
   int v = g_mfma_variant.load(std::memory_order_relaxed);
-  if (v < 0) {
-    v = 0;
+  if (v == -2) {
+    v = kAutoVariant;
     const char* e = std::getenv("PA_MFMA_VARIANT");
     if (e && (e[0] == '0' || e[0] == '1' || e[0] == '2') && e[1] == '\0') v = e[0] - '0';
     g_mfma_variant.store(v, std::memory_order_relaxed);
   }
   return v;
+}
+
+int mfma_variant(const dim3& grid) {
+  const int v = mfma_variant_setting();
+  if (v != kAutoVariant) return v;
+  const long long wgs = (long long)grid.x * grid.y * grid.z;
+  return wgs >= kAutoOneWaveGrid ? 1 : 0;
 }
 
 struct Launch {
@@ -801,7 +813,7 @@ void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
 template <int DT, int D, int G>
 hipError_t launch_attn_t(const AttnArgs& a, const Launch& l) {
   if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
-    switch (mfma_variant()) {
+    switch (mfma_variant(l.grid)) {
       case 0: launch(attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>, l, 2 * 64, a); break;
       case 1: launch(attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>, l, 64, a); break;
       default: launch(attn_mfma_kernel<DT, D, G, 4, 2>, l, 4 * 64, a); break;
@@ -849,12 +861,12 @@ hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
 }  // namespace
 
 int set_mfma_variant(int v) {
-  if (v < 0 || v > 2) return -1;
+  if (v < kAutoVariant || v > 2) return -1;
   g_mfma_variant.store(v, std::memory_order_relaxed);
   return 0;
 }
 
-int get_mfma_variant() { return mfma_variant(); }
+int get_mfma_variant() { return mfma_variant_setting(); }
 
 Kernel kernel_for(int dtype, int group) {
   return (dtype != PA_F32 && group >= 4) ? Kernel::kMfma : Kernel::kValu;

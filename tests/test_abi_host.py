@@ -185,19 +185,30 @@ def test_num_partitions_golden():
     assert B.pa_num_partitions(10, 0) == -1
 
 
-def test_path_threshold():
-    # V1 iff the context bound <= threshold (default 8192 tokens: project_6 commit a2a5dd8 page).
+def test_path_rules():
     old = B.pa_get_v1_max_context()
     try:
+        # Pages' rule (project_6 commit a2a5dd8 page): V1 iff the context bound <= 8192.
         B.pa_set_v1_max_context(8192)
+        assert B.pa_get_v1_max_context() == 8192
         assert B.pa_choose_path(dims(max_blocks_per_seq=512)) == B.PA_PATH_V1      # 8192
         assert B.pa_choose_path(dims(max_blocks_per_seq=513)) == B.PA_PATH_V2      # 8208
         assert B.pa_choose_path(dims(max_blocks_per_seq=6250)) == B.PA_PATH_V2
         assert B.pa_choose_path(dims(max_blocks_per_seq=6250), 4000) == B.PA_PATH_V1
         B.pa_set_v1_max_context(0)
         assert B.pa_choose_path(dims(max_blocks_per_seq=1)) == B.PA_PATH_V2
+        # Measured MI355X rule (default): V1 iff one partition or S*Hkv >= 256.
         B.pa_set_v1_max_context(-5)
-        assert B.pa_get_v1_max_context() == 0
+        assert B.pa_get_v1_max_context() == -1
+        one = dims(num_seqs=1, num_kv_heads=4, max_blocks_per_seq=512)            # 8192 tokens
+        assert B.pa_choose_path(one, 0, 512) == B.PA_PATH_V2
+        assert B.pa_choose_path(one, 512, 512) == B.PA_PATH_V1                    # one partition
+        assert B.pa_choose_path(one, 513, 512) == B.PA_PATH_V2
+        assert B.pa_choose_path(one, 1024, 1024) == B.PA_PATH_V1
+        wide = dims(num_seqs=64, num_kv_heads=4, max_blocks_per_seq=6250)         # 256 KV heads
+        assert B.pa_choose_path(wide, 0, 512) == B.PA_PATH_V1
+        narrow = dims(num_seqs=63, num_kv_heads=4, max_blocks_per_seq=6250)       # 252
+        assert B.pa_choose_path(narrow, 0, 512) == B.PA_PATH_V2
     finally:
         B.pa_set_v1_max_context(old)
 
@@ -205,11 +216,12 @@ def test_path_threshold():
 def test_mfma_variant_knob():
     old = B.pa_get_mfma_variant()
     try:
-        for v in (0, 1, 2):
+        for v in (0, 1, 2, -1):
             B.pa_set_mfma_variant(v)
             assert B.pa_get_mfma_variant() == v
-        with pytest.raises(B.PaError):
-            B.pa_set_mfma_variant(3)
+        for bad in (3, -2):
+            with pytest.raises(B.PaError):
+                B.pa_set_mfma_variant(bad)
     finally:
         B.pa_set_mfma_variant(old)
 

@@ -81,8 +81,8 @@ def test_config_parity(cfg, P, path):
     check_close(to_f64(out), ref, f"{wl.CONFIG_NAMES[cfg]} P={P} path={path}")
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
-@pytest.mark.parametrize("cfg", [2, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, -1])
+@pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_mfma_variants(cfg, variant):
     w, dev, ref = config_case(cfg)
     old = B.pa_get_mfma_variant()
