@@ -203,11 +203,23 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   constexpr int NC = D / 128;    // 16-byte V runs per lane per row
   constexpr int NMM = D / 16;    // PV instructions per block (16 head-dim columns each)
 
+  constexpr int CPR = D / 8;                     // 16-byte chunks per K/V row
+  // K staging through LDS (contiguous global reads, see compute_block) pays at
+  // head_dim 256, where a strided K read touches 16 rows of 512 bytes per instruction
+  // (mixed_d256: 74.4 -> 60.0 us/step); at head_dim 128 it only adds latency.
+  constexpr bool kStageK = D == 256;
+  constexpr int kTileBytes = kStageK ? NW * 16 * CPR * 16 : 16;  // one K tile per wave
+  constexpr int kMergeBytes = (NW > 1 ? NW - 1 : 1) * NMM * 4 * 64 * 4;
   __shared__ u32x4 s_qf[NKK][64];   // query operand, one 16-byte fragment per lane
   __shared__ float s_mref[NW][16];  // per wave and head: reference max of the sums
   __shared__ float s_mmax[NW][16];  // per wave and head: true max logit
   __shared__ float s_l[NW][16];     // per wave and head: exp-sum relative to the reference
-  __shared__ float s_o[NW > 1 ? NW - 1 : 1][NMM * 4][64];
+  // During the block loop: each wave's K tile on its way from the contiguous load layout
+  // to the MFMA operand layout.  After the loop: the other waves' accumulators.
+  __shared__ __attribute__((aligned(16)))
+  unsigned char s_un[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
+  typedef float MergeRows[NMM * 4][64];
+  MergeRows* s_o = reinterpret_cast<MergeRows*>(s_un);
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -262,8 +274,13 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
     const int nbytes = (real && (unsigned)phys < (unsigned)a.NB) ? kBlockSize * D * 2 : 0;
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + (size_t)phys * bstride, nbytes);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + (size_t)phys * bstride, nbytes);
+    // K, staged: instruction j reads bytes [1024 j, 1024 j + 1024) of the tile, one
+    // 16-byte chunk per lane in order -- whole cache lines per instruction.  K, direct:
+    // lane (r16, kg) reads row r16, columns 32 kk + 8 kg .. +7 (the operand layout).
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kr[kk] = ld_stream(rk, (r16 * D + 32 * kk + 8 * kg) * 2);
+    for (int j = 0; j < NKK; ++j)
+      kr[j] = kStageK ? ld_stream(rk, (64 * j + lane) * 16)
+                      : ld_stream(rk, (r16 * D + 32 * j + 8 * kg) * 2);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -278,8 +295,26 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
     int ql = lane;
     asm volatile("" : "+v"(ql));
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kStageK) {
+      // Re-layout K through this wave's LDS tile: chunk (row r, column c) is stored at
+      // slot r*CPR + (c + r) % CPR.  The rotation makes both the contiguous writes and
+      // the operand reads (16 rows, one column) hit distinct banks.
+      u32x4* tile = reinterpret_cast<u32x4*>(s_un) + w * 16 * CPR;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s = mfma_16x16x32<kBF>(kr[kk], s_qf[kk][ql], s);
+      for (int j = 0; j < NKK; ++j) {
+        const int cl = 64 * j + ql;
+        const int r = cl / CPR, c = cl % CPR;
+        tile[r * CPR + (c + r) % CPR] = kr[j];
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 kt = tile[r16 * CPR + (4 * kk + kg + r16) % CPR];
+        s = mfma_16x16x32<kBF>(kt, s_qf[kk][ql], s);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s = mfma_16x16x32<kBF>(kr[kk], s_qf[kk][ql], s);
+    }
     const int valid = pt.ntok - (w + NW * kidx) * kBlockSize;  // >= 1, wave-uniform
     float x[4];
 #pragma unroll
@@ -377,6 +412,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
     s_mmax[w][r16] = m_max;
     s_l[w][r16] = l_run;
   }
+  __syncthreads();  // every wave is done with its K tile (if staged); the bytes become s_o
   if (NW > 1 && w > 0) {
 #pragma unroll
     for (int mm = 0; mm < NMM; ++mm)
