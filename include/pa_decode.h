@@ -108,6 +108,13 @@ pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const voi
  *   tmp_out     [S, Hq, Pmax, D]  normalised partial output of each partition
  *   max_logits  [S, Hq, Pmax]     max over the partition of scale*q.k
  *   exp_sums    [S, Hq, Pmax]     sum over the partition of exp(logit - max)
+ * followed by the piece area of the work split (see pa_set_work_split), with
+ * slots = min(1024, S*Hkv*Pmax*2^s) where 2^s (at most 16) is the largest number
+ * of equal pieces of a multiple of 64 tokens that partition_size divides into
+ * (0 slots if that is 1), G = Hq/Hkv:
+ *   piece_out   [slots, G, D]     normalised partial output of each piece
+ *   piece_max   [slots, G]        max over the piece of scale*q.k
+ *   piece_sum   [slots, G]        sum over the piece of exp(logit - max)
  * pa_workspace_layout() returns the offsets.  The contents need no
  * initialisation.  Returns 0 when the arguments are invalid (see pa_last_error()).
  */
@@ -115,9 +122,10 @@ size_t pa_workspace_bytes(const pa_dims_t* dims, int64_t max_context_len,
                           int32_t partition_size);
 
 /* Workspace layout for these arguments, written to layout[0..PA_LAYOUT_FIELDS-1]:
- * Pmax, then the byte offsets of tmp_out, max_logits and exp_sums, then the
+ * Pmax; the byte offsets of tmp_out, max_logits and exp_sums; the number of
+ * piece slots; the byte offsets of piece_out, piece_max and piece_sum; the
  * total bytes. */
-#define PA_LAYOUT_FIELDS 5
+#define PA_LAYOUT_FIELDS 9
 pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
                                 int32_t partition_size, int64_t* layout);
 
@@ -126,12 +134,17 @@ pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
  * workspace.  path: PA_PATH_AUTO (pa_choose_path's rule), PA_PATH_V1 or PA_PATH_V2.
  * max_context_len: upper bound on every context_lens[b] (<= 0: MB*16); it
  * sizes the partition grid, so a smaller bound means fewer idle work-groups.
- * It must not exceed MB*16; tokens beyond it are not attended.
+ * It must not exceed MB*16.  A context longer than the bound is attended only
+ * over a prefix: its first ceil(max_context_len / partition_size) *
+ * partition_size tokens on V2, its first max_context_len rounded up to a
+ * multiple of 16 on V1.
  * workspace: device memory of >= pa_workspace_bytes(dims, max_context_len,
  * partition_size) bytes, needed only when the path taken is V2 (may be NULL
  * for V1).  V2 enqueues two launches, phase 1 then phase 2; after the call the
- * workspace holds the phase-1 partials (layout above) of every sequence with
- * more than one partition.  Calls that overlap on the same workspace race.
+ * workspace holds the phase-1 partials (layout above) of every partition of a
+ * sequence with more than one partition, except the partitions the work split
+ * cut into pieces: their partial states are in their pieces' slots.  Calls that
+ * overlap on the same workspace race.
  */
 pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_tables,
@@ -232,6 +245,40 @@ const char* pa_version(void);
  * for an unknown variant. */
 pa_status_t pa_set_mfma_variant(int32_t variant);
 int32_t pa_get_mfma_variant(void);
+
+/*
+ * Work split of the V2 path of pa_decode / pa_decode_ex / pa_decode_profiled (a
+ * load-balancing choice of this implementation; the pages fix the partials per
+ * partition, not how the work-groups that produce them are cut).  Phase-1
+ * items are (partition, KV head, sequence), linear index
+ * p + Pmax*(h + Hkv*b), dispatched in that order.  A cut item runs as 2^s
+ * work-groups, piece c covering tokens [p*P + c*P/2^s, p*P + (c+1)*P/2^s), each
+ * writing its (max, exp-sum, normalised output) to a piece slot; phase 2 folds
+ * a cut partition's non-empty pieces in place of its partial (same log-sum-exp
+ * rule, so the output agrees to rounding).  pa_v2_partition / pa_v2_reduce /
+ * pa_v1 never cut.
+ * pieces: -1 automatic (default): with C compute units and W items, cut
+ *            every item into the most pieces that keep W*pieces <= C when
+ *            W < C; else cut the last r = W mod C items (if 0 < r <= C/2)
+ *            into the fewest pieces >= 2 that make r*pieces a multiple of C,
+ *            or, if none does, into the most pieces allowed;
+ *          0 or 1: never cut;
+ *          2, 4, 8, 16: cut every item from first_item on into that many pieces.
+ * The number of pieces is lowered to what partition_size allows (pieces of
+ * a multiple of 64 tokens); if the cut items' pieces exceed the workspace's piece
+ * slots, only the last items that fit are cut.  first_item is used only with a
+ * fixed number of pieces.  Process-wide; returns PA_ERR_UNSUPPORTED for another
+ * pieces value and PA_ERR_SHAPE for a negative first_item.
+ */
+pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item);
+/* Current setting: returns pieces, writes first_item if the pointer is non-NULL. */
+int32_t pa_get_work_split(int64_t* first_item);
+/* Split a V2 call with these arguments would use under the current setting,
+ * written to plan[0..3]: items W, first cut item (W if none), pieces per cut
+ * item (1 if none), phase-1 work-groups.  The automatic setting reads the
+ * current device's compute-unit count (PA_ERR_HIP without a device). */
+pa_status_t pa_split_plan(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size,
+                          int64_t* plan);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -66,7 +66,12 @@ SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_set_mfma_variant": (_I32, [_I32]),
     "pa_get_mfma_variant": (_I32, []),
+    "pa_set_work_split": (_I32, [_I32, _I64]),
+    "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
+    "pa_split_plan": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
 }
+
+LAYOUT_FIELDS = 9
 
 _lib_handle = None
 
@@ -269,18 +274,42 @@ def pa_get_mfma_variant():
     return int(lib().pa_get_mfma_variant())
 
 
+def pa_set_work_split(pieces, first_item=0):
+    """-1 automatic, 0/1 off, 2/4/8/16 pieces for every item from first_item on."""
+    _check(lib().pa_set_work_split(int(pieces), int(first_item)))
+
+
+def pa_get_work_split():
+    """(pieces, first_item) of the current work-split setting."""
+    f = ctypes.c_int64()
+    return int(lib().pa_get_work_split(ctypes.byref(f))), int(f.value)
+
+
+def split_plan(q, k_cache, block_tables, max_context_len=0, partition_size=512):
+    """Work split a V2 call would use: dict items, first, pieces, workgroups."""
+    d = dims_of(q, k_cache, block_tables)
+    v = (ctypes.c_int64 * 4)()
+    _check(lib().pa_split_plan(ctypes.byref(d), int(max_context_len), int(partition_size), v))
+    return dict(zip(("items", "first", "pieces", "workgroups"), list(v)))
+
+
 def workspace_layout(q, k_cache, block_tables, max_context_len=0, partition_size=512):
     """Section offsets of a V2 workspace, as the library computes them.
 
-    Returns a dict: pmax, bytes, and for tmp_out / max_logits / exp_sums a
-    (byte offset, shape) pair; all three are fp32, tmp_out [S, Hq, pmax, D] and
-    the statistics [S, Hq, pmax].
+    Returns a dict: pmax, bytes, slots, and for tmp_out / max_logits / exp_sums /
+    piece_out / piece_max / piece_sum a (byte offset, shape) pair; all are fp32,
+    tmp_out [S, Hq, pmax, D], the statistics [S, Hq, pmax], piece_out
+    [slots, G, D] and the piece statistics [slots, G].
     """
     d = dims_of(q, k_cache, block_tables)
-    v = (ctypes.c_int64 * 5)()
+    v = (ctypes.c_int64 * LAYOUT_FIELDS)()
     _check(lib().pa_workspace_layout(ctypes.byref(d), int(max_context_len),
                                      int(partition_size), v))
-    pmax, o_tmp, o_max, o_sum, nbytes = list(v)
+    pmax, o_tmp, o_max, o_sum, slots, o_pout, o_pmax, o_psum, nbytes = list(v)
     S, Hq, D = d.num_seqs, d.num_q_heads, d.head_dim
-    return {"pmax": pmax, "bytes": nbytes, "tmp_out": (o_tmp, (S, Hq, pmax, D)),
-            "max_logits": (o_max, (S, Hq, pmax)), "exp_sums": (o_sum, (S, Hq, pmax))}
+    G = Hq // d.num_kv_heads
+    return {"pmax": pmax, "bytes": nbytes, "slots": slots,
+            "tmp_out": (o_tmp, (S, Hq, pmax, D)),
+            "max_logits": (o_max, (S, Hq, pmax)), "exp_sums": (o_sum, (S, Hq, pmax)),
+            "piece_out": (o_pout, (slots, G, D)), "piece_max": (o_pmax, (slots, G)),
+            "piece_sum": (o_psum, (slots, G))}

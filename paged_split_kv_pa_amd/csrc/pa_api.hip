@@ -7,6 +7,7 @@
 // calls are hipGetDevice / hipMalloc / hipFree for the library-owned
 // workspace of pa_decode, hipGetLastError after launches, and the launches.
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -55,6 +56,11 @@ pa_status_t fail(pa_status_t st, const char* fmt, ...) {
 
 pa_status_t ok() { return PA_OK; }
 
+pa_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int element_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
@@ -66,8 +72,24 @@ struct Plan {
   int32_t P;          // partition size used by the kernels
   int64_t Pmax;       // partition-grid size
   size_t off_tmp, off_max, off_sum;  // phase-1 partials
+  int64_t piece_slots;               // piece partials of a work split (see pa::Split)
+  size_t off_pout, off_pmax, off_psum;
   size_t ws_bytes;
 };
+
+// Largest piece shift the partition size allows: pieces are whole multiples of four
+// cache blocks (64 tokens; smaller pieces cost more in fixed per-work-group and phase-2
+// work than they save in balance on MI355X), at most 2^kMaxPieceShift of them.
+constexpr int kMinPieceTokens = 4 * pa::kBlockSize;
+int max_piece_shift(int32_t P) {
+  if (P <= 0 || P % kMinPieceTokens) return 0;
+  int m = P / kMinPieceTokens, sh = 0;
+  while (sh < pa::kMaxPieceShift && (m & 1) == 0) {
+    m >>= 1;
+    ++sh;
+  }
+  return sh;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -138,7 +160,98 @@ pa_status_t make_plan(const pa_dims_t* d, int64_t max_context_len, int32_t parti
   pl->off_tmp = 0;
   pl->off_max = align256(rows * pl->D * sizeof(float));
   pl->off_sum = pl->off_max + align256(rows * sizeof(float));
-  pl->ws_bytes = pl->off_sum + align256(rows * sizeof(float));
+  const size_t end = pl->off_sum + align256(rows * sizeof(float));
+  const int msh = need_partition ? max_piece_shift(pl->P) : 0;
+  const int64_t items = (int64_t)pl->S * pl->Hkv * pl->Pmax;
+  pl->piece_slots = msh > 0 ? std::min<int64_t>(pa::kMaxPieceSlots, items << msh) : 0;
+  const size_t prow = (size_t)pl->piece_slots * pl->G;
+  pl->off_pout = end;
+  pl->off_pmax = pl->off_pout + align256(prow * pl->D * sizeof(float));
+  pl->off_psum = pl->off_pmax + align256(prow * sizeof(float));
+  pl->ws_bytes = pl->off_psum + align256(prow * sizeof(float));
+  return ok();
+}
+
+// ---- work split (see pa::Split) --------------------------------------------------------
+// Setting: pieces -1 = automatic, 0 = off, 2..16 = cut every item from first_item on.
+std::atomic<int32_t> g_split_pieces{-1};
+std::atomic<int64_t> g_split_first{0};
+
+// Compute units of the current device (cached per device).
+std::atomic<int> g_cu_count[64];
+
+pa_status_t compute_units(int* ncu) {
+  int dev = 0;
+  pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PA_OK) return st;
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_INTERNAL, "device id %d out of range", dev);
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    st = hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                          "hipDeviceGetAttribute(compute units)");
+    if (st != PA_OK) return st;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  *ncu = n;
+  return ok();
+}
+
+int floor_log2(int64_t x) {
+  int r = -1;
+  while (x > 0) {
+    x >>= 1;
+    ++r;
+  }
+  return r;
+}
+
+// The split of a V2 phase-1 launch.  Automatic rule, with C compute units and W items
+// dispatched round-robin over them (measured on MI355X: a CU's HBM bandwidth is capped
+// far below what the whole device can stream, so the time of a launch follows the
+// most-loaded CUs):
+//   W <  C: every item is cut into the largest 2^s pieces with W * 2^s <= C, so that a
+//           small grid still reaches every compute unit;
+//   W >= C: the last r = W mod C items, if 0 < r <= C/2, are cut into the fewest
+//           2^s >= 2 pieces with r * 2^s a multiple of C, so that every CU ends with
+//           the same load; failing that, into the most pieces allowed.  (With r > C/2
+//           the busy CUs of the last round already draw most of the bandwidth, and a
+//           cut measured slower.)
+pa_status_t plan_split(const Plan& pl, pa::Split* sp) {
+  *sp = pa::Split();
+  const int msh = max_piece_shift(pl.P);
+  const int64_t items = (int64_t)pl.S * pl.Hkv * pl.Pmax;
+  const int32_t mode = g_split_pieces.load(std::memory_order_relaxed);
+  if (msh == 0 || mode == 0 || mode == 1 || items == 0) return ok();
+  int64_t first = 0;
+  int shift = 0;
+  if (mode > 1) {
+    shift = std::min(floor_log2(mode), msh);
+    first = std::min<int64_t>(std::max<int64_t>(g_split_first.load(), 0), items);
+  } else {
+    int ncu = 0;
+    pa_status_t st = compute_units(&ncu);
+    if (st != PA_OK) return st;
+    if (items < ncu) {
+      shift = std::min(floor_log2(ncu / items), msh);
+      first = 0;
+    } else {
+      const int64_t rem = items % ncu;
+      if (rem == 0 || 2 * rem > ncu) return ok();
+      first = items - rem;
+      shift = 0;
+      for (int s = 1; s <= msh && (rem << s) <= pl.piece_slots; ++s) {
+        shift = s;
+        if ((rem << s) % ncu == 0) break;
+      }
+    }
+  }
+  if (shift <= 0) return ok();
+  // Only as many items as the piece area holds are cut (the last ones).
+  first = std::max<int64_t>(first, items - (pl.piece_slots >> shift));
+  if (first >= items) return ok();
+  if (first + ((items - first) << shift) > pa::kMaxSplitGrid) return ok();
+  sp->first = (int32_t)first;
+  sp->shift = shift;
   return ok();
 }
 
@@ -158,14 +271,20 @@ pa_status_t check_scale(float scale) {
   return ok();
 }
 
-pa_status_t hip_status(hipError_t e, const char* what) {
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
-  return ok();
+// The split with its piece-area pointers inside workspace ws.
+pa::Split split_in(const Plan& pl, const pa::Split& sp, const void* ws) {
+  pa::Split r = sp;
+  if (r.shift == 0 || !ws) return pa::Split();
+  char* base = static_cast<char*>(const_cast<void*>(ws));
+  r.piece_out = reinterpret_cast<float*>(base + pl.off_pout);
+  r.piece_max = reinterpret_cast<float*>(base + pl.off_pmax);
+  r.piece_sum = reinterpret_cast<float*>(base + pl.off_psum);
+  return r;
 }
 
 pa::AttnArgs attn_args(const Plan& pl, void* out, const void* q, const void* k, const void* v,
-                       const int32_t* bt, const int32_t* ctx, float scale, void* ws) {
+                       const int32_t* bt, const int32_t* ctx, float scale, void* ws,
+                       const pa::Split& sp) {
   pa::AttnArgs a;
   a.out = out;
   a.q = q;
@@ -184,20 +303,21 @@ pa::AttnArgs attn_args(const Plan& pl, void* out, const void* q, const void* k, 
   a.MB = pl.MB;
   a.P = pl.P;
   a.Pmax = (int32_t)pl.Pmax;
+  a.split = split_in(pl, sp, ws);
   return a;
 }
 
 pa_status_t run_partition(const pa_dims_t* dims, const Plan& pl, void* out, const void* q,
                           const void* k, const void* v, const int32_t* bt, const int32_t* ctx,
-                          float scale, void* ws, hipStream_t st, hipEvent_t e0 = nullptr,
-                          hipEvent_t e1 = nullptr) {
-  pa::AttnArgs a = attn_args(pl, out, q, k, v, bt, ctx, scale, ws);
+                          float scale, void* ws, hipStream_t st, const pa::Split& sp,
+                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  pa::AttnArgs a = attn_args(pl, out, q, k, v, bt, ctx, scale, ws, sp);
   return hip_status(pa::launch_attention(dims->dtype, pl.D, pl.G, a, pl.S, st, e0, e1),
                     "attention kernel launch");
 }
 
 pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const int32_t* ctx,
-                       const void* ws, hipStream_t st) {
+                       const void* ws, hipStream_t st, const pa::Split& sp) {
   pa::ReduceArgs r;
   const char* base = static_cast<const char*>(ws);
   r.out = out;
@@ -206,9 +326,11 @@ pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const i
   r.max_logits = reinterpret_cast<const float*>(base + pl.off_max);
   r.exp_sums = reinterpret_cast<const float*>(base + pl.off_sum);
   r.Hq = pl.Hq;
+  r.Hkv = pl.Hkv;
   r.MB = pl.MB;
   r.P = pl.P;
   r.Pmax = (int32_t)pl.Pmax;
+  r.split = split_in(pl, sp, ws);
   return hip_status(pa::launch_reduce(dims->dtype, pl.D, r, pl.S, st), "phase-2 reduce launch");
 }
 
@@ -267,7 +389,8 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   if (take == PA_PATH_V1) {
     Plan p1;
     if ((st = make_plan(dims, max_context_len, 0, false, &p1)) != PA_OK) return st;
-    return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs, e0, e1);
+    return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs, pa::Split(), e0,
+                         e1);
   }
   if (owned) {
     if ((st = owned_workspace(pl.ws_bytes, &workspace)) != PA_OK) return st;
@@ -279,10 +402,12 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
                   workspace_bytes, pl.ws_bytes);
     if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
-  if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs, e0, e1)) !=
+  pa::Split sp;
+  if ((st = plan_split(pl, &sp)) != PA_OK) return st;
+  if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs, sp, e0, e1)) !=
       PA_OK)
     return st;
-  return run_reduce(dims, pl, out, ctx, workspace, hs);
+  return run_reduce(dims, pl, out, ctx, workspace, hs, sp);
 }
 
 }  // namespace
@@ -314,8 +439,15 @@ pa_status_t pa_workspace_layout(const pa_dims_t* dims, int64_t max_context_len,
   Plan pl;
   pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
   if (st != PA_OK) return st;
-  const int64_t v[PA_LAYOUT_FIELDS] = {pl.Pmax, (int64_t)pl.off_tmp, (int64_t)pl.off_max,
-                                       (int64_t)pl.off_sum, (int64_t)pl.ws_bytes};
+  const int64_t v[PA_LAYOUT_FIELDS] = {pl.Pmax,
+                                       (int64_t)pl.off_tmp,
+                                       (int64_t)pl.off_max,
+                                       (int64_t)pl.off_sum,
+                                       pl.piece_slots,
+                                       (int64_t)pl.off_pout,
+                                       (int64_t)pl.off_pmax,
+                                       (int64_t)pl.off_psum,
+                                       (int64_t)pl.ws_bytes};
   for (int i = 0; i < PA_LAYOUT_FIELDS; ++i) layout[i] = v[i];
   return ok();
 }
@@ -367,7 +499,7 @@ pa_status_t pa_v2_partition(const pa_dims_t* dims, void* out, const void* q,
                 workspace_bytes, pl.ws_bytes);
   if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
   return run_partition(dims, pl, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                       workspace, static_cast<hipStream_t>(stream));
+                       workspace, static_cast<hipStream_t>(stream), pa::Split());
 }
 
 pa_status_t pa_v2_reduce(const pa_dims_t* dims, void* out, const int32_t* context_lens,
@@ -384,7 +516,8 @@ pa_status_t pa_v2_reduce(const pa_dims_t* dims, void* out, const int32_t* contex
     return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu needed", workspace,
                 workspace_bytes, pl.ws_bytes);
   if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  return run_reduce(dims, pl, out, context_lens, workspace, static_cast<hipStream_t>(stream));
+  return run_reduce(dims, pl, out, context_lens, workspace, static_cast<hipStream_t>(stream),
+                    pa::Split());
 }
 
 pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
@@ -399,7 +532,7 @@ pa_status_t pa_v1(const pa_dims_t* dims, void* out, const void* q, const void* k
     return st;
   if ((st = check_scale(scale)) != PA_OK) return st;
   return run_partition(dims, pl, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                       nullptr, static_cast<hipStream_t>(stream));
+                       nullptr, static_cast<hipStream_t>(stream), pa::Split());
 }
 
 int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size) {
@@ -444,5 +577,38 @@ pa_status_t pa_set_mfma_variant(int32_t variant) {
 }
 
 int32_t pa_get_mfma_variant(void) { return pa::get_mfma_variant(); }
+
+pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item) {
+  if (pieces != -1 && pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4 && pieces != 8 &&
+      pieces != 16)
+    return fail(PA_ERR_UNSUPPORTED, "work split of %d pieces unknown (-1, 0, 1, 2, 4, 8, 16)",
+                pieces);
+  if (first_item < 0) return fail(PA_ERR_SHAPE, "first_item %lld is negative",
+                                  (long long)first_item);
+  g_split_first.store(first_item);
+  g_split_pieces.store(pieces);
+  return ok();
+}
+
+int32_t pa_get_work_split(int64_t* first_item) {
+  if (first_item) *first_item = g_split_first.load();
+  return g_split_pieces.load();
+}
+
+pa_status_t pa_split_plan(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size,
+                          int64_t* plan) {
+  if (!plan) return fail(PA_ERR_NULL, "plan is NULL");
+  Plan pl;
+  pa_status_t st = make_plan(dims, max_context_len, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  pa::Split sp;
+  if ((st = plan_split(pl, &sp)) != PA_OK) return st;
+  const int64_t items = (int64_t)pl.S * pl.Hkv * pl.Pmax;
+  plan[0] = items;
+  plan[1] = sp.shift ? sp.first : items;
+  plan[2] = (int64_t)1 << sp.shift;
+  plan[3] = sp.shift ? sp.first + ((items - sp.first) << sp.shift) : items;
+  return ok();
+}
 
 }  // extern "C"

@@ -10,7 +10,26 @@ namespace pa {
 
 constexpr int kBlockSize = 16;   // tokens per KV-cache block
 constexpr int kWaves = 4;        // waves per attention work-group
-constexpr int kMaxReducePartitions = 8192;  // phase-2 weights live in LDS (32 KB)
+constexpr int kMaxReducePartitions = 8192;  // partition-grid limit per sequence
+constexpr int kMaxPieceShift = 4;           // a split item has at most 16 pieces
+constexpr int kMaxPieceSlots = 1024;        // piece partials the workspace holds
+constexpr int64_t kMaxSplitGrid = 1 << 24;  // linear (split) grids stay below this
+
+// Work split for load balance.  Grid items are (partition p, KV head g, sequence b)
+// with linear index p + Pmax * (g + Hkv * b), the order in which work-groups are
+// dispatched.  Items from split_first on are each cut into 2^split_shift pieces of
+// P >> split_shift tokens, one work-group per piece, on a one-dimensional grid of
+// split_first + (items - split_first) << split_shift work-groups.  A piece writes its
+// (max, exp-sum, normalised output) per query head to slot (work-group index -
+// split_first) of the piece area; phase 2 folds a split partition's pieces in place
+// of its row of the partials.  split_shift == 0: no split, grid (Pmax, Hkv, S).
+struct Split {
+  int32_t first = 0;
+  int32_t shift = 0;
+  float* piece_out = nullptr;   // [slots][G][D]
+  float* piece_max = nullptr;   // [slots][G], natural-log units like max_logits
+  float* piece_sum = nullptr;   // [slots][G]
+};
 
 // Arguments of the attention kernel (phase 1 and V1 share it).
 struct AttnArgs {
@@ -27,6 +46,7 @@ struct AttnArgs {
   int32_t Hq, Hkv, NB, MB;
   int32_t P;                 // tokens per partition (multiple of 16)
   int32_t Pmax;              // partition-grid size
+  Split split;
 };
 
 // Arguments of the phase-2 (cross-partition) kernel.
@@ -36,7 +56,8 @@ struct ReduceArgs {
   const float* tmp_out;
   const float* max_logits;
   const float* exp_sums;
-  int32_t Hq, MB, P, Pmax;
+  int32_t Hq, Hkv, MB, P, Pmax;
+  Split split;
 };
 
 // Work-group shape of the matrix-core kernel (-1 automatic, 0, 1 or 2; see
@@ -48,7 +69,8 @@ int get_mfma_variant();
 enum class Kernel { kMfma, kValu };
 Kernel kernel_for(int dtype, int group);
 
-// Launch the attention kernel on grid (Pmax, Hkv, S).  Returns the launch status.
+// Launch the attention kernel on grid (Pmax, Hkv, S), or on the linear grid of a split
+// (see Split).  Returns the launch status.
 // ev_start / ev_stop (may be null) are recorded when the kernel starts / ends.
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
                             hipStream_t stream, hipEvent_t ev_start = nullptr,

@@ -151,26 +151,78 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 }
 
 // ---- work-group set-up shared by both attention kernels ------------------------------
+// The grid item of this work-group (see Split): partition p of KV head g of sequence b,
+// whole (piece < 0) or one of its pieces.
+struct Item {
+  int p, g, b, piece;
+};
+
+__device__ __forceinline__ Item grid_item(const AttnArgs& a) {
+  Item it;
+  it.piece = -1;
+  if (a.split.shift == 0) {
+    it.p = blockIdx.x;
+    it.g = blockIdx.y;
+    it.b = blockIdx.z;
+    return it;
+  }
+  int j = blockIdx.x;
+  if (j >= a.split.first) {
+    const int t = j - a.split.first;
+    j = a.split.first + (t >> a.split.shift);
+    it.piece = t & ((1 << a.split.shift) - 1);
+  }
+  it.p = j % a.Pmax;
+  const int r = j / a.Pmax;
+  it.g = r % a.Hkv;
+  it.b = r / a.Hkv;
+  return it;
+}
+
 struct Part {
   int n;       // context length (clamped to the table capacity)
   int nparts;  // partitions of this sequence that exist in the grid
-  int tok0;    // first token of this partition
-  int ntok;    // tokens in this partition
-  int nblk;    // cache blocks in this partition
+  int tok0;    // first token of this work-group's range
+  int ntok;    // tokens in the range (<= 0: an empty piece of the last partition)
+  int nblk;    // cache blocks in the range
 };
 
-__device__ __forceinline__ Part plan_partition(const AttnArgs& a, int b, int p) {
+__device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it) {
   Part r;
-  int n = a.ctx[b];
+  int n = a.ctx[it.b];
   const int cap = a.MB * kBlockSize;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int np = (n + a.P - 1) / a.P;
   r.n = n;
   r.nparts = np > a.Pmax ? a.Pmax : np;
-  r.tok0 = p * a.P;
-  r.ntok = min(a.P, n - r.tok0);
+  int len = a.P;
+  r.tok0 = it.p * a.P;
+  if (it.piece >= 0) {
+    len = a.P >> a.split.shift;
+    r.tok0 += it.piece * len;
+  }
+  r.ntok = min(len, n - r.tok0);
   r.nblk = (r.ntok + kBlockSize - 1) / kBlockSize;
   return r;
+}
+
+// Rows of the partial state of query head h of this work-group's group: the
+// partition's row of tmp_out / max_logits / exp_sums, or the piece's slot.
+template <int G, int D>
+__device__ __forceinline__ void partial_rows(const AttnArgs& a, const Item& it, int h, float*& o,
+                                             float*& m, float*& s) {
+  size_t row;
+  if (it.piece >= 0) {
+    row = (size_t)(blockIdx.x - a.split.first) * G + h;
+    o = a.split.piece_out + row * D;
+    m = a.split.piece_max + row;
+    s = a.split.piece_sum + row;
+  } else {
+    row = ((size_t)it.b * a.Hq + (size_t)it.g * G + h) * a.Pmax + it.p;
+    o = a.tmp_out + row * D;
+    m = a.max_logits + row;
+    s = a.exp_sums + row;
+  }
 }
 
 // A sequence with no cached tokens attends to nothing: its output is 0.
@@ -221,17 +273,19 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   typedef float MergeRows[NMM * 4][64];
   MergeRows* s_o = reinterpret_cast<MergeRows*>(s_un);
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const Item it = grid_item(a);
+  const int g = it.g, b = it.b;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // token row (K loads), head column (Q, S), V column run
   const int kg = lane >> 4;   // k-group of the MFMA operands
 
-  const Part pt = plan_partition(a, b, p);
-  if (p >= pt.nparts) {
-    if (p == 0) write_zero_group<DT, D, G>(a, b, g);
+  const Part pt = plan_partition(a, it);
+  if (it.p >= pt.nparts) {
+    if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
     return;
   }
+  if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
   const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
   const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
 
@@ -437,7 +491,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
     }
   };
 
-  const bool single = pt.nparts == 1;
+  const bool single = pt.nparts == 1 && it.piece < 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * kg + i;
@@ -446,6 +500,8 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
     head_stats(h, fac, Mt, L);
     const float linv = 1.f / L;
     const size_t qh = (size_t)b * a.Hq + (size_t)g * G + h;
+    float *po, *pm, *ps;
+    partial_rows<G, D>(a, it, h, po, pm, ps);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       float vals[8];
@@ -461,15 +517,16 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
       if (single)
         store_out<DT, 8>(a.out, qh * D + d0, vals);
       else
-        store_f32<8>(a.tmp_out + (qh * a.Pmax + p) * D + d0, vals);
+        store_f32<8>(po + d0, vals);
     }
   }
   if (!single && kg == 0 && r16 < G) {
     float fac[NW], Mt, L;
     head_stats(r16, fac, Mt, L);
-    const size_t idx = ((size_t)b * a.Hq + (size_t)g * G + r16) * a.Pmax + p;
-    a.max_logits[idx] = Mt * kLn2;
-    a.exp_sums[idx] = L;
+    float *po, *pm, *ps;
+    partial_rows<G, D>(a, it, r16, po, pm, ps);
+    *pm = Mt * kLn2;
+    *ps = L;
   }
 }
 
@@ -527,17 +584,19 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   float* s_p = reinterpret_cast<float*>(smem + kQBytes);   // [kWaves][16][G]
   float* s_o = reinterpret_cast<float*>(smem);             // [kWaves-1][G*VE][64] after it
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const Item it = grid_item(a);
+  const int g = it.g, b = it.b;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int t = lane >> 2, r = lane & 3;
 
-  const Part pt = plan_partition(a, b, p);
-  if (p >= pt.nparts) {
-    if (p == 0) write_zero_group<DT, D, G>(a, b, g);
+  const Part pt = plan_partition(a, it);
+  if (it.p >= pt.nparts) {
+    if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
     return;
   }
+  if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
   const int kcount = w < pt.nblk ? (pt.nblk - w + kWaves - 1) / kWaves : 0;
   const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
 
@@ -702,7 +761,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   __syncthreads();
   if (w != 0) return;
 
-  const bool single = pt.nparts == 1;
+  const bool single = pt.nparts == 1 && it.piece < 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float Mt = s_mmax[0][h];
@@ -729,12 +788,14 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
     if (single) {
       store_out<DT, VE>(a.out, qh * D + lane * VE, vals);
     } else {
-      float* dst = a.tmp_out + (qh * a.Pmax + p) * D + lane * VE;
+      float *po, *pm, *ps;
+      partial_rows<G, D>(a, it, h, po, pm, ps);
+      float* dst = po + lane * VE;
       if constexpr (VE == 2) *reinterpret_cast<f32x2*>(dst) = f32x2{vals[0], vals[1]};
       else store_f32<VE>(dst, vals);
       if (lane == 0) {
-        a.max_logits[qh * a.Pmax + p] = Mt * kLn2;
-        a.exp_sums[qh * a.Pmax + p] = L;
+        *pm = Mt * kLn2;
+        *ps = L;
       }
     }
   }
@@ -763,23 +824,54 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int nparts = (n + a.P - 1) / a.P;
   if (nparts > a.Pmax) nparts = a.Pmax;
-  if (nparts <= 1) return;  // phase 1 wrote the final output (or zeros)
+
+  // Partials to fold: partitions [0, p_split) from their rows, then, for each split
+  // partition, its non-empty pieces from the piece area (see Split).  With no split
+  // p_split == nparts.
+  const int hq = bh - b * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const int gq = hq % G;
+  int p_split = nparts, nfold = nparts, slot0 = 0;
+  const int sh = a.split.shift;
+  if (sh > 0) {
+    const long long item0 = (long long)a.Pmax * ((long long)(hq / G) + (long long)a.Hkv * b);
+    const long long first = (long long)a.split.first - item0;
+    p_split = first <= 0 ? 0 : (first >= nparts ? nparts : (int)first);
+    if (p_split < nparts) {
+      const int sub = a.P >> sh;
+      // Tokens of the last partition; a context beyond the planning bound (nparts
+      // clamped to Pmax) still has at most P there, hence at most 2^sh pieces.
+      const int last_tok = min(a.P, n - (nparts - 1) * a.P);
+      nfold = p_split + ((nparts - 1 - p_split) << sh) + (last_tok + sub - 1) / sub;
+      slot0 = (int)((item0 + p_split - a.split.first) << sh);  // first piece of p_split
+    }
+  }
+  if (p_split == nparts && nparts <= 1) return;  // phase 1 wrote the final output (or zeros)
 
   const size_t base = (size_t)bh * a.Pmax;
-  const float* src = a.tmp_out + base * D + chunk * 32 + d4 * 4;
-  float M = kNegInf, S = 0.f;  // base-2 running max and exp-sum of this thread's partitions
+  const int col = chunk * 32 + d4 * 4;
+  float M = kNegInf, S = 0.f;  // base-2 running max and exp-sum of this thread's partials
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-  for (int q = pg; q < nparts; q += 32) {
-    const float mq = a.max_logits[base + q] * kLog2e;
-    const float sq = a.exp_sums[base + q];
-    const f32x4 oq = *reinterpret_cast<const f32x4*>(src + (size_t)q * D);
-    const float Mn = fmaxf(M, mq);
-    const float c_old = exp2_fast(M - Mn);   // 0 when M is -inf
-    const float c_new = exp2_fast(mq - Mn) * sq;
+  for (int q = pg; q < nfold; q += 32) {
+    // Pieces of consecutive split partitions occupy consecutive slots, so the piece
+    // index q - p_split is the slot offset from the first piece of partition p_split.
+    const bool whole = q < p_split;
+    const size_t row = whole ? base + q : (size_t)(slot0 + q - p_split) * G + gq;
+    const float* mrow = whole ? a.max_logits : a.split.piece_max;
+    const float* srow = whole ? a.exp_sums : a.split.piece_sum;
+    const float* orow = whole ? a.tmp_out : a.split.piece_out;
+    const float mq = mrow[row] * kLog2e;
+    const float sq = srow[row];
+    const f32x4 oq = *reinterpret_cast<const f32x4*>(orow + row * D + col);
+    // The state with the larger max keeps factor 1 exactly (written as a select, so no
+    // fused multiply-add can leave a rounding error in an exp2(0)).
+    const bool up = mq > M;
+    const float c_old = up ? exp2_fast(M - mq) : 1.f;   // 0 when M is -inf
+    const float c_new = (up ? 1.f : exp2_fast(mq - M)) * sq;
     S = S * c_old + c_new;
     acc = acc * c_old + oq * c_new;
-    M = Mn;
+    M = up ? mq : M;
   }
   if (d4 == 0) {
     s_m[pg] = M;
@@ -910,7 +1002,15 @@ Kernel kernel_for(int dtype, int group) {
 
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const Launch l{dim3(a.Pmax, a.Hkv, num_seqs), stream, ev_start, ev_stop};
+  dim3 grid(a.Pmax, a.Hkv, num_seqs);
+  if (a.split.shift > 0) {
+    const long long items = (long long)a.Pmax * a.Hkv * num_seqs;
+    const long long wgs = a.split.first + ((items - a.split.first) << a.split.shift);
+    if (a.split.first < 0 || a.split.first > items || wgs > kMaxSplitGrid)
+      return hipErrorInvalidValue;
+    grid = dim3((unsigned)wgs, 1, 1);
+  }
+  const Launch l{grid, stream, ev_start, ev_stop};
   switch (dtype) {
     case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, a, l);
     case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, a, l);

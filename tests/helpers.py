@@ -1,5 +1,6 @@
 """Helpers shared by the GPU tests: device upload of seeded workloads and the
 tolerance check against the float64 oracle."""
+import contextlib
 import numpy as np
 
 from paged_split_kv_pa_amd import workloads as wl
@@ -65,3 +66,15 @@ def check_close(got, ref, what=""):
 def small_workload(seed, ctx, Hq, Hkv, D, dtype, **kw):
     return wl.make_workload("case", seed, context_lens=ctx, num_q_heads=Hq, num_kv_heads=Hkv,
                             head_dim=D, dtype=dtype, **kw)
+
+
+@contextlib.contextmanager
+def work_split(pieces, first_item=0):
+    """Run the block with the library's work-split setting changed, then restore it."""
+    from paged_split_kv_pa_amd import binding as B
+    old = B.pa_get_work_split()
+    B.pa_set_work_split(pieces, first_item)
+    try:
+        yield
+    finally:
+        B.pa_set_work_split(*old)

@@ -13,6 +13,8 @@ import pytest
 
 from paged_split_kv_pa_amd import binding as B
 
+import split_rule
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa_decode.h")
 
@@ -111,25 +113,36 @@ def test_empty_batch_is_a_no_op():
 
 
 def layout(d, hint, P):
-    v = (ctypes.c_int64 * 5)()
+    v = (ctypes.c_int64 * B.LAYOUT_FIELDS)()
     assert B.lib().pa_workspace_layout(ctypes.byref(d), hint, P, v) == 0
     return list(v)
 
 
 def test_workspace_bytes_layout():
-    d = dims(num_seqs=3, max_blocks_per_seq=100)  # capacity 1600 tokens
+    d = dims(num_seqs=3, max_blocks_per_seq=100)  # capacity 1600 tokens, 4 KV heads
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    for hint, P, pmax in ((0, 512, 4), (513, 512, 2), (0, 16, 100)):
+    # (hint, P, Pmax, piece slots): pieces are multiples of 64 tokens, at most 16, so
+    # P = 512 cuts into up to 8 pieces, 1024 into 16, 64 and 96 not at all; slots =
+    # min(1024, items * pieces).
+    for hint, P, pmax, slots in ((0, 512, 4, 384), (513, 512, 2, 192), (16, 512, 1, 96),
+                                 (0, 16, 100, 0), (0, 96, 17, 0), (64, 64, 1, 0),
+                                 (0, 64, 25, 0), (0, 256, 7, 336), (0, 128, 13, 312),
+                                 (0, 1024, 2, 384)):
+        assert split_rule.piece_slots(3 * 4 * pmax, P) == slots
         rows = 3 * 32 * pmax
         off_max = a256(rows * 128 * 4)
         off_sum = off_max + a256(rows * 4)
-        total = off_sum + a256(rows * 4)
-        assert layout(d, hint, P) == [pmax, 0, off_max, off_sum, total]
+        off_pout = off_sum + a256(rows * 4)
+        off_pmax = off_pout + a256(slots * 8 * 128 * 4)
+        off_psum = off_pmax + a256(slots * 8 * 4)
+        total = off_psum + a256(slots * 8 * 4)
+        assert layout(d, hint, P) == [pmax, 0, off_max, off_sum, slots, off_pout, off_pmax,
+                                      off_psum, total]
         assert B.lib().pa_workspace_bytes(ctypes.byref(d), hint, P) == total
     # Invalid: hint above capacity, bad partition size, NULL output.
     assert B.lib().pa_workspace_bytes(ctypes.byref(d), 1601, 512) == 0
     assert B.lib().pa_workspace_bytes(ctypes.byref(d), 0, 24) == 0
-    v = (ctypes.c_int64 * 5)()
+    v = (ctypes.c_int64 * B.LAYOUT_FIELDS)()
     assert B.lib().pa_workspace_layout(ctypes.byref(d), 0, 24, v) == -5
     assert B.lib().pa_workspace_layout(ctypes.byref(d), 0, 512, None) == -1
 
@@ -226,6 +239,90 @@ def test_mfma_variant_knob():
         B.pa_set_mfma_variant(old)
 
 
+def test_work_split_knob():
+    old = B.pa_get_work_split()
+    try:
+        for pieces, first in ((-1, 0), (0, 0), (1, 3), (2, 0), (4, 7), (8, 1 << 40), (16, 5)):
+            B.pa_set_work_split(pieces, first)
+            assert B.pa_get_work_split() == (pieces, first)
+        for bad in (3, -2, 32, 6):
+            with pytest.raises(B.PaError):
+                B.pa_set_work_split(bad, 0)
+        with pytest.raises(B.PaError):
+            B.pa_set_work_split(4, -1)
+        assert B.pa_get_work_split() == (16, 5)  # a rejected call changes nothing
+    finally:
+        B.pa_set_work_split(*old)
+
+
+def split_plan(d, hint, P):
+    v = (ctypes.c_int64 * 4)()
+    st = B.lib().pa_split_plan(ctypes.byref(d), hint, P, v)
+    return st, list(v)
+
+
+@pytest.mark.parametrize("S,Hkv,MB,hint,P,pieces,first", [
+    (1, 4, 6250, 0, 512, 8, 768),       # long context: cut the 16 tail items
+    (1, 4, 6250, 0, 512, 16, 768),      # P = 512 allows at most 8 pieces
+    (1, 4, 6250, 0, 512, 8, 0),         # every item: only the last 128 fit 1024 slots
+    (1, 4, 6250, 0, 1024, 16, 0),       # P = 1024: 16 pieces of 64 tokens
+    (2, 8, 513, 0, 512, 4, 200),        # cut starts inside a (sequence, head) row
+    (3, 4, 100, 0, 512, 8, 0),
+    (3, 4, 100, 0, 256, 16, 0),         # P = 256 allows at most 4 pieces
+    (3, 4, 100, 0, 128, 16, 0),         # P = 128: 2 pieces of 64 tokens
+    (3, 4, 100, 0, 64, 2, 0),           # P = 64 cannot be cut
+    (3, 4, 100, 0, 96, 4, 0),           # P = 96 is not a multiple of 64
+    (3, 4, 100, 0, 16, 2, 0),
+    (3, 4, 100, 0, 512, 2, 1000),       # first beyond the items: no cut
+    (1, 1, 4, 0, 512, 16, 0),
+])
+def test_split_plan_fixed_pieces(S, Hkv, MB, hint, P, pieces, first):
+    old = B.pa_get_work_split()
+    try:
+        B.pa_set_work_split(pieces, first)
+        d = dims(num_seqs=S, num_q_heads=8 * Hkv, num_kv_heads=Hkv, max_blocks_per_seq=MB)
+        st, got = split_plan(d, hint, P)
+        assert st == 0, B.pa_last_error()
+        pmax = -(-(hint if hint > 0 else MB * 16) // P)
+        items = S * Hkv * pmax
+        assert got == [items, *split_rule.plan(items, P, pieces, first)]
+        assert got[3] <= (1 << 24)
+        if got[2] > 1:
+            assert (items - got[1]) * got[2] <= layout(d, hint, P)[4]  # fits the slots
+        B.pa_set_work_split(0, 0)
+        assert split_plan(d, hint, P)[1] == [items, items, 1, items]
+    finally:
+        B.pa_set_work_split(*old)
+
+
+def test_split_rule_examples():
+    # The automatic rule on 256 compute units.
+    assert split_rule.plan(784, 512, -1, ncu=256) == (768, 8, 896)     # 100K tokens, 4 KV heads
+    assert split_rule.plan(768, 512, -1, ncu=256) == (768, 1, 768)     # balanced already
+    assert split_rule.plan(832, 512, -1, ncu=256) == (768, 4, 1024)    # remainder 64
+    assert split_rule.plan(896, 512, -1, ncu=256) == (768, 2, 1024)    # remainder 128
+    assert split_rule.plan(960, 512, -1, ncu=256) == (960, 1, 960)     # remainder 192 > 128
+    assert split_rule.plan(868, 512, -1, ncu=256) == (768, 8, 1568)    # 100: no multiple
+    assert split_rule.plan(64, 512, -1, ncu=256) == (0, 4, 256)        # 8K tokens, 4 KV heads
+    assert split_rule.plan(2, 512, -1, ncu=256) == (0, 8, 16)
+    assert split_rule.plan(200, 512, -1, ncu=256) == (200, 1, 200)     # 256/200 < 2
+    assert split_rule.plan(64, 64, -1, ncu=256) == (64, 1, 64)         # P = 64: no pieces
+    assert split_rule.plan(8192, 512, -1, ncu=256) == (8192, 1, 8192)  # 32 per CU
+    assert split_rule.plan(257, 256, -1, ncu=256) == (256, 4, 260)     # P = 256: at most 4
+
+
+def test_split_plan_automatic_needs_a_device():
+    old = B.pa_get_work_split()
+    try:
+        B.pa_set_work_split(-1, 0)
+        st, got = split_plan(dims(num_seqs=1, max_blocks_per_seq=6250), 0, 512)
+        assert st in (0, -8)  # -8 (PA_ERR_HIP) where no device is visible
+        if st == 0:
+            assert got[0] == 784 and got[3] >= 784
+    finally:
+        B.pa_set_work_split(*old)
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 4, 128)
@@ -243,3 +340,6 @@ def test_workspace_layout_helper_matches_library():
     lay = B.workspace_layout(q, k, bt, 0, 512)
     d = B.dims_of(q, k, bt)
     assert lay["bytes"] == B.lib().pa_workspace_bytes(ctypes.byref(d), 0, 512)
+    assert lay["slots"] == split_rule.piece_slots(3 * 4 * 4, 512) == 384
+    assert lay["piece_out"][1] == (384, 8, 128)
+    assert lay["piece_sum"][0] + 384 * 8 * 4 <= lay["bytes"]

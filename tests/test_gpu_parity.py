@@ -14,7 +14,7 @@ import oracle
 from paged_split_kv_pa_amd import binding as B
 from paged_split_kv_pa_amd import workloads as wl
 
-from helpers import check_close, small_workload, to_f64, upload
+from helpers import check_close, small_workload, to_f64, upload, work_split
 
 pytestmark = pytest.mark.gpu
 
@@ -247,13 +247,15 @@ def test_runs_are_bitwise_deterministic(cfg):
 
 def test_pa_decode_equals_its_two_phases():
     """pa_decode (library workspace) == pa_decode_ex V2 == pa_v2_partition + pa_v2_reduce,
-    bit for bit, and within tolerance of the oracle."""
+    bit for bit with the work split off (the phase entry points never cut), and within
+    tolerance of the oracle."""
     w, dev, ref = config_case(2)
     say("pa_decode vs pa_decode_ex vs the two phases on long_100k")
     out1 = torch.empty_like(dev["q"])
-    B.pa_decode(out1, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                dev["context_lens"], w.scale, 512)
-    out0 = run_path(w, dev, B.PA_PATH_V2, 512)
+    with work_split(0):
+        B.pa_decode(out1, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                    dev["context_lens"], w.scale, 512)
+        out0 = run_path(w, dev, B.PA_PATH_V2, 512)
     lay = B.workspace_layout(dev["q"], dev["k_cache"], dev["block_tables"], 0, 512)
     ws = torch.empty(lay["bytes"], dtype=torch.uint8, device="cuda")
     out2 = torch.empty_like(dev["q"])
@@ -290,14 +292,21 @@ def test_workspace_reuse_across_shapes():
 
 
 def test_context_hint_and_side_stream():
+    """A context hint only trims idle work-groups: same bits as without it (work split
+    off: the hint changes the item count, hence which items an automatic split cuts)."""
     w, dev, ref = config_case(3)
     say("context hint + side stream on batched_256")
     hint = int(w.context_lens.max())
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        out = run_path(w, dev, B.PA_PATH_V2, 512, max_context_len=hint)
+        auto = run_path(w, dev, B.PA_PATH_V2, 512, max_context_len=hint)
     s.synchronize()
-    check_close(to_f64(out), ref, "hinted")
-    full = run_path(w, dev, B.PA_PATH_V2, 512)
+    check_close(to_f64(auto), ref, "hinted, automatic split")
+    with work_split(0):
+        with torch.cuda.stream(s):
+            out = run_path(w, dev, B.PA_PATH_V2, 512, max_context_len=hint)
+        s.synchronize()
+        check_close(to_f64(out), ref, "hinted")
+        full = run_path(w, dev, B.PA_PATH_V2, 512)
     assert torch.equal(out, full)
 
