@@ -123,6 +123,9 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, const float* v)
   }
 }
 
+// Partial states use plain stores: they are read back by the next kernel, and
+// non-temporal stores measured slower for both kernels (phase 1 37.3 -> 39.7 us at
+// 100K tokens).
 template <int N>
 __device__ __forceinline__ void store_f32(float* dst, const float* v) {
 #pragma unroll
@@ -803,97 +806,173 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
 
 // =======================================================================================
 // Phase 2: cross-partition log-sum-exp merge.
-// Grid (S*Hq, D/32); 256 threads = 32 partition lanes x 8 float4 columns.
+// Grid (S*Hq, kReduceChunks); 256 threads.  Per (sequence, head): M = max of the partial maxima,
+// r_q = exp(m_q - M) * s_q per partial state q, out = sum_q r_q o_q / sum_q r_q.
 // =======================================================================================
+constexpr int kMaxFold = kMaxReducePartitions + kMaxPieceSlots;  // partial states per head
+// Phase 2 splits each head's D columns over 8 work-groups: D/8 columns each (16 at
+// head_dim 128: 64 partition lanes x 4 float4 column lanes).  Phase 2 is bound by
+// per-CU load issue, so more, narrower work-groups finish sooner -- as long as the
+// grid stays small: at head_dim 256 with 16 columns its speculative loads cost more
+// than they save (measured).
+constexpr int kReduceChunks = 8;
+
 template <int DT, int D>
 __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
-  // Thread (pg, d4): partition lane pg (32 of them) and 4 of the 32 columns of this
-  // work-group.  Each thread folds its partitions pg, pg+32, ... with the running
-  // log-sum-exp rule; the partitions' loads do not depend on each other, so the
-  // whole partial set is requested in one memory round trip.  The 32 lanes are then
-  // folded in a fixed order (bitwise deterministic).
-  __shared__ float s_m[32], s_s[32];
-  __shared__ f32x4 s_acc[32][8];
+  // The weights r_q live in LDS (one per partial state); thread (pg, d4) then sums
+  // r_q o_q over its partial states q = pg, pg+NPG, ... for 4 of the work-group's
+  // kReduceCols columns, and the NPG partition lanes are summed in a fixed tree
+  // (bitwise deterministic).
+  constexpr int kReduceCols = D / kReduceChunks;
+  constexpr int NC4 = kReduceCols / 4;  // float4 column lanes
+  constexpr int NPG = 256 / NC4;        // partition lanes
+  __shared__ float s_w[kMaxFold];
+  __shared__ float s_red[4];
+  __shared__ f32x4 s_acc[4][NC4];
   const int bh = blockIdx.x, chunk = blockIdx.y;
   const int b = bh / a.Hq;
   const int tid = threadIdx.x;
-  const int d4 = tid & 7, pg = tid >> 3;
+  const int d4 = tid % NC4, pg = tid / NC4;
+  const int lane = tid & 63, wv = tid >> 6;
+
+  // Partial states to fold, in order: partitions [0, p_split) from their rows, then, for
+  // each cut partition (see Split), its non-empty pieces from consecutive piece slots.
+  // The list of any context is a prefix of the nominal list of a context that fills the
+  // whole partition grid, and every entry of the nominal list lies inside the workspace.
+  // So the first loads are issued together with the context-length load (one memory
+  // round trip instead of two) and masked once it is known.
+  const int hq = bh - b * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const int gq = hq % G;
+  const int sh = a.split.shift;
+  int nom_split = a.Pmax, nom_fold = a.Pmax, slot0 = 0;
+  if (sh > 0) {
+    const long long item0 = (long long)a.Pmax * ((long long)(hq / G) + (long long)a.Hkv * b);
+    const long long first = (long long)a.split.first - item0;
+    nom_split = first <= 0 ? 0 : (first >= a.Pmax ? a.Pmax : (int)first);
+    nom_fold = nom_split + ((a.Pmax - nom_split) << sh);
+    if (nom_split < a.Pmax) slot0 = (int)((item0 + nom_split - a.split.first) << sh);
+  }
+  const long long base = (long long)bh * a.Pmax;
+  const int col = chunk * kReduceCols + d4 * 4;
+  // Piece rows are addressed as element offsets from the partition arrays (both live in
+  // one workspace), so an entry selects an integer, not a pointer: a selected pointer
+  // argument is fetched from the argument segment by the compiler, a dependent load.
+  const float* const mls = a.max_logits;
+  const float* const ess = a.exp_sums;
+  const float* const tmp = a.tmp_out;
+  const long long dm = sh ? (long long)(a.split.piece_max - mls) : 0;
+  const long long ds = sh ? (long long)(a.split.piece_sum - ess) : 0;
+  const long long dO = sh ? (long long)(a.split.piece_out - tmp) : 0;
+  auto prow = [&](int q) { return (long long)(slot0 + q - nom_split) * G + gq; };
+  auto load_o = [&](int q) {
+    const long long io = q < nom_split ? (base + q) * D : dO + prow(q) * D;
+    return *reinterpret_cast<const f32x4*>(tmp + io + col);
+  };
+  auto load_ms = [&](int q, float& m, float& s) {
+    const bool whole = q < nom_split;
+    m = mls[whole ? base + q : dm + prow(q)];
+    s = ess[whole ? base + q : ds + prow(q)];
+  };
+
+  // Unconditional loads (an index past the nominal list re-reads its last entry), and
+  // no arithmetic on them before the context length is known: a guarded or consumed
+  // load would make the compiler wait for it before issuing the next one.
+  // Output rows per thread (states pg + NPG i) loaded up front: 320 states cover the
+  // 196 partitions of a 100K-token context plus its cut items' pieces.
+  constexpr int kSpecO = 320 / NPG;
+  constexpr int kSpecMS = 2;  // statistics per thread: partial states tid + 256 j
+  f32x4 so[kSpecO];
+  float sm[kSpecMS], ss[kSpecMS];
+#pragma unroll
+  for (int j = 0; j < kSpecMS; ++j) load_ms(min(tid + 256 * j, nom_fold - 1), sm[j], ss[j]);
+#pragma unroll
+  for (int i = 0; i < kSpecO; ++i) so[i] = load_o(min(pg + NPG * i, nom_fold - 1));
 
   int n = a.ctx[b];
   const int cap = a.MB * kBlockSize;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int nparts = (n + a.P - 1) / a.P;
   if (nparts > a.Pmax) nparts = a.Pmax;
-
-  // Partials to fold: partitions [0, p_split) from their rows, then, for each split
-  // partition, its non-empty pieces from the piece area (see Split).  With no split
-  // p_split == nparts.
-  const int hq = bh - b * a.Hq;
-  const int G = a.Hq / a.Hkv;
-  const int gq = hq % G;
-  int p_split = nparts, nfold = nparts, slot0 = 0;
-  const int sh = a.split.shift;
-  if (sh > 0) {
-    const long long item0 = (long long)a.Pmax * ((long long)(hq / G) + (long long)a.Hkv * b);
-    const long long first = (long long)a.split.first - item0;
-    p_split = first <= 0 ? 0 : (first >= nparts ? nparts : (int)first);
-    if (p_split < nparts) {
-      const int sub = a.P >> sh;
-      // Tokens of the last partition; a context beyond the planning bound (nparts
-      // clamped to Pmax) still has at most P there, hence at most 2^sh pieces.
-      const int last_tok = min(a.P, n - (nparts - 1) * a.P);
-      nfold = p_split + ((nparts - 1 - p_split) << sh) + (last_tok + sub - 1) / sub;
-      slot0 = (int)((item0 + p_split - a.split.first) << sh);  // first piece of p_split
-    }
+  const int p_split = nom_split < nparts ? nom_split : nparts;
+  int nfold = nparts;
+  if (p_split < nparts) {
+    const int sub = a.P >> sh;
+    // Tokens of the last partition; a context beyond the planning bound (nparts
+    // clamped to Pmax) still has at most P there, hence at most 2^sh pieces.
+    const int last_tok = min(a.P, n - (nparts - 1) * a.P);
+    nfold = p_split + ((nparts - 1 - p_split) << sh) + (last_tok + sub - 1) / sub;
   }
   if (p_split == nparts && nparts <= 1) return;  // phase 1 wrote the final output (or zeros)
 
-  const size_t base = (size_t)bh * a.Pmax;
-  const int col = chunk * 32 + d4 * 4;
-  float M = kNegInf, S = 0.f;  // base-2 running max and exp-sum of this thread's partials
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int q = pg; q < nfold; q += 32) {
-    // Pieces of consecutive split partitions occupy consecutive slots, so the piece
-    // index q - p_split is the slot offset from the first piece of partition p_split.
-    const bool whole = q < p_split;
-    const size_t row = whole ? base + q : (size_t)(slot0 + q - p_split) * G + gq;
-    const float* mrow = whole ? a.max_logits : a.split.piece_max;
-    const float* srow = whole ? a.exp_sums : a.split.piece_sum;
-    const float* orow = whole ? a.tmp_out : a.split.piece_out;
-    const float mq = mrow[row] * kLog2e;
-    const float sq = srow[row];
-    const f32x4 oq = *reinterpret_cast<const f32x4*>(orow + row * D + col);
-    // The state with the larger max keeps factor 1 exactly (written as a select, so no
-    // fused multiply-add can leave a rounding error in an exp2(0)).
-    const bool up = mq > M;
-    const float c_old = up ? exp2_fast(M - mq) : 1.f;   // 0 when M is -inf
-    const float c_new = (up ? 1.f : exp2_fast(mq - M)) * sq;
-    S = S * c_old + c_new;
-    acc = acc * c_old + oq * c_new;
-    M = up ? mq : M;
+  // Base-2 maxima into LDS; block max M.  The weights below read the maxima back from
+  // LDS, so exp2(m_q - M) is exactly 1 for the largest (no fused multiply-add can keep
+  // the rounding error of m * log2(e)).
+  float mx = kNegInf;
+  auto put_max = [&](int q, float m) {
+    const float m2 = m * kLog2e;
+    s_w[q] = m2;
+    mx = fmaxf(mx, m2);
+  };
+#pragma unroll
+  for (int j = 0; j < kSpecMS; ++j)
+    if (tid + 256 * j < nfold) put_max(tid + 256 * j, sm[j]);
+  for (int q = tid + 256 * kSpecMS; q < nfold; q += 256) {
+    float m, s;
+    load_ms(q, m, s);
+    put_max(q, m);
   }
-  if (d4 == 0) {
-    s_m[pg] = M;
-    s_s[pg] = S;
-  }
-  s_acc[pg][d4] = acc;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+  if (lane == 0) s_red[wv] = mx;
   __syncthreads();
-  if (tid < 8) {
-    float Mt = s_m[0];
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  // Weights r_q = exp2(m_q - M) * s_q, and their sum.
+  float wsum = 0.f;
 #pragma unroll
-    for (int i = 1; i < 32; ++i) Mt = fmaxf(Mt, s_m[i]);
-    float St = 0.f;
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float c = s_m[i] == kNegInf ? 0.f : exp2_fast(s_m[i] - Mt);
-      St += c * s_s[i];
-      tot += c * s_acc[i][tid];
+  for (int j = 0; j < kSpecMS; ++j) {
+    const int q = tid + 256 * j;
+    if (q < nfold) {
+      const float r = exp2_fast(s_w[q] - M) * ss[j];
+      s_w[q] = r;
+      wsum += r;
     }
-    const float inv = 1.f / St;
-    const float vals[4] = {tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
-    store_out<DT, 4>(a.out, (size_t)bh * D + chunk * 32 + tid * 4, vals);
+  }
+  for (int q = tid + 256 * kSpecMS; q < nfold; q += 256) {
+    float m, s;
+    load_ms(q, m, s);
+    const float r = exp2_fast(s_w[q] - M) * s;
+    s_w[q] = r;
+    wsum += r;
+  }
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) wsum += __shfl_xor(wsum, x);
+  __syncthreads();  // weights visible; s_red reads of M done
+  if (lane == 0) s_red[wv] = wsum;
+
+  // sum_q r_q o_q over this thread's partial states.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kSpecO; ++i)
+    if (pg + NPG * i < nfold) acc += so[i] * s_w[pg + NPG * i];
+#pragma unroll 4
+  for (int q = pg + NPG * kSpecO; q < nfold; q += NPG) acc += load_o(q) * s_w[q];
+
+  // Lanes NC4 apart in a wave hold the same columns: shuffle steps sum a wave's
+  // partition lanes, then the 4 waves meet in LDS.
+#pragma unroll
+  for (int x = NC4; x < 64; x <<= 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], x);
+  if (lane < NC4) s_acc[wv][d4] = acc;
+  __syncthreads();
+  if (tid < NC4) {
+    const float total = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    const f32x4 o = (s_acc[0][d4] + s_acc[1][d4]) + (s_acc[2][d4] + s_acc[3][d4]);
+    const float inv = 1.f / total;
+    const float vals[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    store_out<DT, 4>(a.out, (size_t)bh * D + chunk * kReduceCols + tid * 4, vals);
   }
 }
 
@@ -975,10 +1054,10 @@ template <int DT>
 hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
   dim3 block(256);
   if (D == 128) {
-    dim3 grid((unsigned)(S * a.Hq), 128 / 32);
+    dim3 grid((unsigned)(S * a.Hq), kReduceChunks);
     hipLaunchKernelGGL((reduce_kernel<DT, 128>), grid, block, 0, st, a);
   } else if (D == 256) {
-    dim3 grid((unsigned)(S * a.Hq), 256 / 32);
+    dim3 grid((unsigned)(S * a.Hq), kReduceChunks);
     hipLaunchKernelGGL((reduce_kernel<DT, 256>), grid, block, 0, st, a);
   } else {
     return hipErrorInvalidValue;
