@@ -20,6 +20,8 @@ Sources (the pages are cited by title and section; no line numbers):
   two phases.
 * project_6 commit a2a5dd8 ("computility-run.yaml" commit page), decode-path
   summary -- the V1/V2 context-length thresholds.
+* project_6_baseline5 GROUND_TRUTH_STATUS_v2.md, section "路径 3" -- the
+  prefix-caching cache copy kernel (``cache_ops``).
 
 Modules:
 
@@ -27,6 +29,7 @@ Modules:
 * ``attention`` -- the unpartitioned definition (``decode_attention``), the
   literal two-phase statement (``partitioned_decode``), the partial-statistics
   merge (``merge_partials``) and the partition arithmetic.
+* ``cache_ops`` -- the KV block copy of prefix caching (``copy_blocks``).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute force and invariants (see each function's docstring).
@@ -42,3 +45,4 @@ from .attention import (  # noqa: F401
     num_partitions,
     gather_sequence,
 )
+from .cache_ops import copy_blocks  # noqa: F401
