@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--sweep-paths", action="store_true",
                     help="time forced V1 against forced V2 over a grid of batch sizes and "
                          "context lengths (32/4 heads, head_dim 128, bf16) and exit")
+    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
+                    help="decode (the headline) or the prefix-caching KV block copy")
+    ap.add_argument("--pairs", type=int, default=2048,
+                    help="copy_blocks: (src, dst) block pairs per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference "
                          "kernel for scaling hardware byte counters), then exit")
@@ -175,6 +179,133 @@ def sweep_paths(steps=40, warmup=5):
     return rows
 
 
+def bench_copy_blocks(args):
+    """The prefix-caching block copy (pa_copy_blocks) on the long_100k pool shape: 7500
+    blocks of 4 KV heads x 16 x 128 bf16 per pool, `--pairs` disjoint (src, dst) pairs
+    drawn with a fixed seed; pool replicas rotate so that the copied blocks are cold."""
+    import ctypes
+    import torch
+    import oracle
+    from paged_split_kv_pa_amd import binding as B
+
+    NB, Hkv, D = 7500, 4, 128
+    n = args.pairs
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(NB)[:2 * n]
+    pairs_np = np.stack([ids[:n], ids[n:]], axis=1).astype(np.int32)
+    pool_bytes = 2 * NB * Hkv * 16 * D * 2
+    R = args.copies if args.copies > 0 else max(2, -(-(1 << 30) // pool_bytes))
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    ks = [torch.randn(NB, Hkv, 16, D, device="cuda", dtype=torch.bfloat16, generator=gen)
+          for _ in range(R)]
+    vs = [torch.randn(NB, Hkv, 16, D, device="cuda", dtype=torch.bfloat16, generator=gen)
+          for _ in range(R)]
+    pairs = torch.from_numpy(pairs_np).cuda()
+    block_bytes = Hkv * 16 * D * 2
+    algo_bytes = 2 * 2 * n * block_bytes  # K and V, read once and written once
+    lib = B.lib()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    call_args = [[ctypes.c_void_p(ks[c].data_ptr()), ctypes.c_void_p(vs[c].data_ptr()),
+                  block_bytes, NB, ctypes.c_void_p(pairs.data_ptr()), n, sptr] for c in range(R)]
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+
+    def step(i):
+        st = lib.pa_copy_blocks(*call_args[i % R])
+        if st != 0:
+            raise B.PaError(st, B.pa_last_error())
+
+    # parity of the first call against the oracle on a sample of pairs
+    k0, v0 = ks[0].clone(), vs[0].clone()
+    step(0)
+    torch.cuda.synchronize()
+    sample = pairs_np[:64]
+    want_k, _ = oracle.copy_blocks(k0.view(torch.int16).cpu().numpy(),
+                                   v0.view(torch.int16).cpu().numpy(), sample)
+    got_k = ks[0].view(torch.int16).cpu().numpy()
+    parity_ok = bool(np.array_equal(got_k[sample[:, 1]], want_k[sample[:, 1]]))
+    del k0, v0
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i % max(1, args.event_every) == 0:
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(e0))
+            hip.hipEventCreate(ctypes.byref(e1))
+            hip.hipEventRecord(e0, sptr)
+            step(i)
+            hip.hipEventRecord(e1, sptr)
+            evs.append((e0, e1))
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ctypes.c_float()
+    ker = []
+    for e0, e1 in evs:
+        hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1)
+        ker.append(ms.value * 1e3)
+        hip.hipEventDestroy(e0)
+        hip.hipEventDestroy(e1)
+    us = wall * 1e6 / args.steps
+    kmean = float(np.mean(ker))
+    # Reference: a plain contiguous device-to-device copy of the same byte count (read +
+    # write), cold source rotated the same way: what the hardware gives for a copy.
+    half = algo_bytes // 2
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dst = torch.empty(half, dtype=torch.uint8, device="cuda")
+    for i in range(5):
+        dst.copy_(srcs[i % R])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(50):
+        dst.copy_(srcs[i % R])
+    torch.cuda.synchronize()
+    plain_us = (time.perf_counter() - t1) * 1e6 / 50
+    del srcs, dst
+    log(f"copy_blocks: {n} pairs, {algo_bytes / 1e6:.1f} MB moved per call; call {us:.2f} us; "
+        f"kernel (event pair) mean {kmean:.2f} us, median {np.median(ker):.2f}")
+    rec = {
+        "metric": "KV block copy GB/s (bytes read + written) + us/call, prefix-caching copy",
+        "value": round(algo_bytes / (us / 1e6) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "us_per_step": round(us, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"copy_blocks_{n}", "num_blocks": NB, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": 16, "pairs": n, "block_bytes": block_bytes,
+                   "bytes_per_call": algo_bytes, "pool_copies": R},
+        "roofline": {"bound": "hbm", "achieved": round(algo_bytes / (kmean / 1e6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(algo_bytes / (kmean / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "copy_blocks_kernel",
+                     "kernel_mean_us": round(kmean, 3), "kernel_samples": len(ker)},
+        "parity": {"sampled_pairs_bitwise": parity_ok},
+        "plain_copy_reference": {"bytes": algo_bytes, "us": round(plain_us, 3),
+                                 "GBps": round(algo_bytes / (plain_us / 1e6) / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        kc = ks[0].view(torch.int16).cpu().numpy()
+        vc = vs[0].view(torch.int16).cpu().numpy()
+        reps, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 10.0):
+            oracle.copy_blocks(kc, vc, pairs_np)
+            reps += 1
+        el = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": round(algo_bytes * reps / el / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} full calls (numpy gather of every block "
+                                         f"pair into copies of both pools), {el:.1f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +319,11 @@ def main():
         return
     if args.sweep_paths:
         sweep_paths()
+        return
+    if args.op == "copy_blocks":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        bench_copy_blocks(args)
         return
 
     from paged_split_kv_pa_amd import binding as B

@@ -280,6 +280,28 @@ int32_t pa_get_work_split(int64_t* first_item);
 pa_status_t pa_split_plan(const pa_dims_t* dims, int64_t max_context_len, int32_t partition_size,
                           int64_t* plan);
 
+/*
+ * pa_copy_blocks -- KV-cache block copy of prefix caching (copy-on-write of a
+ * shared block).  Source: project_6_baseline5 GROUND_TRUTH_STATUS_v2.md, section
+ * "路径 3" (prefix caching on; its cache copy kernel named as not optimised).
+ * For each pair i of block_pairs ([num_pairs][2] int32 on the device: src, dst),
+ * block dst of k_cache (and of v_cache) becomes a bitwise copy of block src.
+ * A block of one pool is block_bytes contiguous bytes (Hkv*16*D*element bytes
+ * in the [num_blocks, Hkv, 16, D] layout); num_blocks bounds both ids.
+ * v_cache may be NULL (K pool only).  Pointers: device memory owned by the
+ * caller; k_cache / v_cache 16-byte aligned, block_pairs 4-byte aligned.
+ * A pair with an id outside [0, num_blocks) is skipped (nothing is written).
+ * Pairs are copied in parallel: destinations must be distinct and must not be
+ * among the sources (identity pairs aside), otherwise the result is
+ * unspecified (but nothing outside the listed dst blocks is written).
+ * Asynchronous on stream; num_pairs == 0 is a no-op.  Returns PA_ERR_SHAPE for
+ * block_bytes not a positive multiple of 16 (or >= 2^31), num_blocks outside
+ * [1, 2^31) or num_pairs < 0; PA_ERR_NULL / PA_ERR_ALIGN for pointers;
+ * PA_ERR_HIP if the launch fails.
+ */
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, int64_t num_blocks,
+                           const int32_t* block_pairs, int64_t num_pairs, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -69,6 +69,7 @@ SIGNATURES = {
     "pa_set_work_split": (_I32, [_I32, _I64]),
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
     "pa_split_plan": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
+    "pa_copy_blocks": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P]),
 }
 
 LAYOUT_FIELDS = 9
@@ -291,6 +292,24 @@ def split_plan(q, k_cache, block_tables, max_context_len=0, partition_size=512):
     v = (ctypes.c_int64 * 4)()
     _check(lib().pa_split_plan(ctypes.byref(d), int(max_context_len), int(partition_size), v))
     return dict(zip(("items", "first", "pieces", "workgroups"), list(v)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy blocks src -> dst of both pools (v_cache may be None) for the (src, dst)
+    int32 rows of ``block_pairs`` [n, 2]; all device tensors."""
+    for t in (k_cache, v_cache, block_pairs):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise PaError(-1, "pa_copy_blocks takes contiguous device tensors")
+    if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
+        raise PaError(-3, "v_cache must match k_cache in shape and dtype")
+    if block_pairs.dtype.itemsize != 4 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise PaError(-3, "block_pairs must be an int32 tensor [n, 2]")
+    block_bytes = k_cache[0].numel() * k_cache.element_size()
+    _check(lib().pa_copy_blocks(ctypes.c_void_p(k_cache.data_ptr()),
+                                ctypes.c_void_p(v_cache.data_ptr() if v_cache is not None else 0),
+                                int(block_bytes), int(k_cache.shape[0]),
+                                ctypes.c_void_p(block_pairs.data_ptr()), int(block_pairs.shape[0]),
+                                _stream(stream)))
 
 
 def workspace_layout(q, k_cache, block_tables, max_context_len=0, partition_size=512):

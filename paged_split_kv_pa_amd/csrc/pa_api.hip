@@ -578,6 +578,41 @@ pa_status_t pa_set_mfma_variant(int32_t variant) {
 
 int32_t pa_get_mfma_variant(void) { return pa::get_mfma_variant(); }
 
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, int64_t num_blocks,
+                           const int32_t* block_pairs, int64_t num_pairs, void* stream) {
+  try {
+    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %lld is negative", (long long)num_pairs);
+    if (block_bytes <= 0 || block_bytes % 16 || block_bytes > (int64_t)0x7fffffff)
+      return fail(PA_ERR_SHAPE, "block_bytes %lld must be a positive multiple of 16 below 2^31",
+                  (long long)block_bytes);
+    if (num_blocks <= 0 || num_blocks > (int64_t)0x7fffffff)
+      return fail(PA_ERR_SHAPE, "num_blocks %lld must be in [1, 2^31)", (long long)num_blocks);
+    if (num_pairs == 0) return ok();
+    if (!k_cache || !block_pairs)
+      return fail(PA_ERR_NULL, "k_cache (%p) and block_pairs (%p) must not be NULL", k_cache,
+                  (const void*)block_pairs);
+    if (!aligned16(k_cache) || (v_cache && !aligned16(v_cache)))
+      return fail(PA_ERR_ALIGN, "k_cache and v_cache must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(block_pairs) & 3u)
+      return fail(PA_ERR_ALIGN, "block_pairs must be 4-byte aligned");
+    pa::CopyArgs a;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.pairs = block_pairs;
+    a.block_bytes = (int32_t)block_bytes;
+    a.num_blocks = (int32_t)num_blocks;
+    a.chunks = (int32_t)((block_bytes + pa::copy_chunk_bytes() - 1) / pa::copy_chunk_bytes());
+    if (num_pairs * a.chunks >= (int64_t)0x7fffffff)
+      return fail(PA_ERR_UNSUPPORTED, "%lld pairs of %d chunks exceed the grid limit",
+                  (long long)num_pairs, a.chunks);
+    return hip_status(pa::launch_copy_blocks(a, num_pairs, v_cache != nullptr,
+                                             static_cast<hipStream_t>(stream)),
+                      "block-copy launch");
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
 pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item) {
   if (pieces != -1 && pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4 && pieces != 8 &&
       pieces != 16)

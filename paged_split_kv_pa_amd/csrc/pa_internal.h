@@ -79,4 +79,18 @@ hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& 
 hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
                          hipStream_t stream);
 
+// ---- KV block copy (pa_copy.hip) ------------------------------------------------------
+struct CopyArgs {
+  void* k;                   // K pool: num_blocks blocks of block_bytes bytes
+  void* v;                   // V pool (same shape), or null for a K-only copy
+  const int32_t* pairs;      // [num_pairs][2] (src, dst) block ids
+  int32_t block_bytes;       // bytes of one block of one pool (multiple of 16)
+  int32_t num_blocks;
+  int32_t chunks;            // work-groups per block: ceil(block_bytes / copy_chunk_bytes())
+};
+int copy_chunk_bytes();
+// Grid (num_pairs * chunks, 1 or 2 pools).
+hipError_t launch_copy_blocks(const CopyArgs& a, long long num_pairs, bool with_v,
+                              hipStream_t stream);
+
 }  // namespace pa

@@ -343,3 +343,19 @@ def test_workspace_layout_helper_matches_library():
     assert lay["slots"] == split_rule.piece_slots(3 * 4 * 4, 512) == 384
     assert lay["piece_out"][1] == (384, 8, 128)
     assert lay["piece_sum"][0] + 384 * 8 * 4 <= lay["bytes"]
+
+
+def test_copy_blocks_validation():
+    lib = B.lib()
+    K, V, PR = FAKE[0], FAKE[1], FAKE[2]
+    assert lib.pa_copy_blocks(None, None, 4096, 10, None, 0, None) == 0  # no pairs: no-op
+    for bb in (0, -16, 24, 1 << 31):
+        assert lib.pa_copy_blocks(K, V, bb, 10, PR, 1, None) == -3
+    assert lib.pa_copy_blocks(K, V, 4096, 0, PR, 1, None) == -3
+    assert lib.pa_copy_blocks(K, V, 4096, 10, PR, -1, None) == -3
+    assert lib.pa_copy_blocks(None, V, 4096, 10, PR, 1, None) == -1
+    assert lib.pa_copy_blocks(K, V, 4096, 10, None, 1, None) == -1
+    assert lib.pa_copy_blocks(ctypes.c_void_p(0x10008), V, 4096, 10, PR, 1, None) == -4
+    assert lib.pa_copy_blocks(K, ctypes.c_void_p(0x10008), 4096, 10, PR, 1, None) == -4
+    assert lib.pa_copy_blocks(K, V, 4096, 10, ctypes.c_void_p(0x10002), 1, None) == -4
+    assert "block_pairs" in B.pa_last_error()
