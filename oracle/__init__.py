@@ -22,6 +22,9 @@ Sources (the pages are cited by title and section; no line numbers):
   summary -- the V1/V2 context-length thresholds.
 * project_6_baseline5 GROUND_TRUTH_STATUS_v2.md, section "路径 3" -- the
   prefix-caching cache copy kernel (``cache_ops``).
+* project_6 optimizations/prefix_prefill_patch.py (commit fee8f1b) docstring and
+  the "Dockerfile" commit page, "What CAN be optimized" -- the prefix-prefill
+  attention kernel (``prefill``).
 
 Modules:
 
@@ -30,6 +33,8 @@ Modules:
   literal two-phase statement (``partitioned_decode``), the partial-statistics
   merge (``merge_partials``) and the partition arithmetic.
 * ``cache_ops`` -- the KV block copy of prefix caching (``copy_blocks``).
+* ``prefill`` -- paged prefix-prefill attention (``prefill_attention``) and its
+  FLOP count.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute force and invariants (see each function's docstring).
@@ -46,3 +51,4 @@ from .attention import (  # noqa: F401
     gather_sequence,
 )
 from .cache_ops import copy_blocks  # noqa: F401
+from .prefill import prefill_attention, prefill_rows, prefill_flops  # noqa: F401

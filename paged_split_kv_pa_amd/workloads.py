@@ -242,3 +242,123 @@ def kv_bytes(context_lens, num_kv_heads, head_dim, dtype):
     """
     n = int(np.sum(np.asarray(context_lens, dtype=np.int64)))
     return n * int(num_kv_heads) * 2 * int(head_dim) * ELEMENT_BYTES[dtype]
+
+
+# ---- paged prefix-prefill inputs ------------------------------------------------------
+@dataclass
+class PrefillWorkload:
+    """Inputs of one prefix-prefill step: a chunk of new tokens per sequence (packed q /
+    k_new / v_new over the batch) after a prefix already in the paged cache.
+
+    Layouts: q [T, Hq, D]; k_new, v_new [T, Hkv, D]; k_cache, v_cache [NB, Hkv, 16, D];
+    block_tables int32 [S, MB] (prefix blocks; padding points at ``pad_block``);
+    context_lens int32 [S] (prefix lengths); query_start int32 [S+1] (sequence b owns
+    rows query_start[b] .. query_start[b+1]-1)."""
+    name: str
+    dtype: str
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    query_start: np.ndarray
+    scale: float
+    pad_block: int
+    seed: int
+
+    @property
+    def num_seqs(self):
+        return self.context_lens.shape[0]
+
+    @property
+    def num_tokens(self):
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self):
+        return self.q.shape[1]
+
+    @property
+    def num_kv_heads(self):
+        return self.k_new.shape[1]
+
+    @property
+    def head_dim(self):
+        return self.q.shape[2]
+
+    @property
+    def max_query_len(self):
+        return int(np.max(np.diff(self.query_start))) if self.num_seqs else 0
+
+
+def make_prefill_workload(name, seed, *, context_lens, query_lens, num_q_heads, num_kv_heads,
+                          head_dim, dtype, sigma=1.0, scale=None, pool_factor=1.2):
+    """Draw one seeded prefill step.  Draw order: q, k_new, v_new, K pool, V pool, block
+    permutation; values N(0, sigma^2) in float32, rounded once to the storage dtype."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    ql = np.asarray(query_lens, dtype=np.int64)
+    S = ctx.shape[0]
+    if ql.shape[0] != S:
+        raise ValueError("one query length per sequence")
+    T = int(ql.sum())
+    Hq, Hkv, D = int(num_q_heads), int(num_kv_heads), int(head_dim)
+    nblk = [-(-int(c) // BLOCK_SIZE) for c in ctx]
+    MB = max(1, max(nblk) if S else 1)
+    used = int(sum(nblk))
+    NB = max(used + 1, int(math.ceil(used * pool_factor)) + 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    q = to_storage(rng.standard_normal((T, Hq, D), dtype=np.float32) * sigma, dtype)
+    k_new = to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32) * sigma, dtype)
+    v_new = to_storage(rng.standard_normal((T, Hkv, D), dtype=np.float32) * sigma, dtype)
+    k_cache = to_storage(rng.standard_normal((NB, Hkv, BLOCK_SIZE, D), dtype=np.float32) * sigma,
+                         dtype)
+    v_cache = to_storage(rng.standard_normal((NB, Hkv, BLOCK_SIZE, D), dtype=np.float32) * sigma,
+                         dtype)
+    perm = rng.permutation(NB)
+    pad_block = int(perm[used])
+    bt = np.full((max(S, 0), MB), pad_block, dtype=np.int32)
+    o = 0
+    for b in range(S):
+        bt[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    qs = np.zeros(S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(ql)
+    return PrefillWorkload(name=name, dtype=dtype, q=q, k_new=k_new, v_new=v_new,
+                           k_cache=k_cache, v_cache=v_cache, block_tables=bt,
+                           context_lens=ctx.astype(np.int32), query_start=qs,
+                           scale=float(np.float32(scale)), pad_block=pad_block, seed=seed)
+
+
+def _pf_small(seed=10):
+    # 3 sequences: no prefix, a prefix ending mid-block, a 200-token prefix; GQA 4.
+    return make_prefill_workload("pf_small", seed, context_lens=[0, 37, 200],
+                                 query_lens=[17, 64, 5], num_q_heads=8, num_kv_heads=2,
+                                 head_dim=128, dtype="bf16")
+
+
+def _pf_chunk(seed=11):
+    # One 8192-token prefill chunk (the pages' max-num-batched-tokens) after a 65536-token
+    # cached prefix; 32/4 heads, head_dim 128, bf16.
+    return make_prefill_workload("pf_chunk_8k_at_64k", seed, context_lens=[65536],
+                                 query_lens=[8192], num_q_heads=32, num_kv_heads=4,
+                                 head_dim=128, dtype="bf16")
+
+
+def _pf_batch(seed=12):
+    # 4 sequences of mixed prefix and chunk lengths, GQA 8, fp16.
+    return make_prefill_workload("pf_batch_mixed", seed, context_lens=[4096, 0, 1000, 16384],
+                                 query_lens=[1024, 2048, 333, 512], num_q_heads=32,
+                                 num_kv_heads=4, head_dim=128, dtype="f16")
+
+
+PREFILL_CONFIGS = {0: _pf_small, 1: _pf_chunk, 2: _pf_batch}
+PREFILL_CONFIG_NAMES = {0: "pf_small", 1: "pf_chunk_8k_at_64k", 2: "pf_batch_mixed"}
+
+
+def prefill_config(i):
+    """Prefill workload ``i`` (seed = 10 + i)."""
+    return PREFILL_CONFIGS[i]()
