@@ -302,6 +302,52 @@ pa_status_t pa_split_plan(const pa_dims_t* dims, int64_t max_context_len, int32_
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, int64_t num_blocks,
                            const int32_t* block_pairs, int64_t num_pairs, void* stream);
 
+/*
+ * Paged prefix-prefill attention.  Source: project_6
+ * optimizations/prefix_prefill_patch.py (commit fee8f1b), docstring: the
+ * prefix_prefill kernel, Flash-Attention style over query tiles and K/V tiles,
+ * fp16/bf16, head_dim 128, GQA; and the "Dockerfile" commit page (project_6 commit
+ * 96f4baf), "What CAN be optimized", items 1-2 (the same kernel; prefill chunks).
+ * What it computes (the plainest reading of the pages): sequence b has a prefix of
+ * c_b = context_lens[b] tokens in the paged cache (block_tables as in decode) and a
+ * chunk of L_b = query_start[b+1] - query_start[b] new tokens, packed over the batch
+ * in q [T, Hq, D], k_new / v_new [T, Hkv, D].  New token i attends, with decode's
+ * softmax attention, to the c_b prefix tokens and to new tokens 0..i (causal):
+ *   out[query_start[b] + i, h, :] = sum_j softmax_j(scale * <q, k_j>) v_j.
+ * The new tokens' K/V are read from k_new / v_new only (writing them into the cache
+ * is a separate step).  Layouts and dtypes as in decode; out [T, Hq, D] in q's dtype.
+ * Built: fp16 and bf16, head_dim 128, block_size 16, Hq/Hkv in {1, 2, 4, 8, 16}
+ * (others: PA_ERR_UNSUPPORTED).  query_start must be non-decreasing from 0 with
+ * query_start[S] <= T (rows past T are not read or written); a context length is
+ * clamped to MB*16.  max_query_len bounds every L_b and sizes the grid (<= 0: T);
+ * a longer chunk is computed only for its first max_query_len tokens.
+ */
+typedef struct pa_prefill_dims {
+  int32_t num_seqs;            /* S */
+  int32_t num_tokens;          /* T: rows of q, k_new, v_new and out */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv */
+  int32_t head_dim;            /* D */
+  int32_t block_size;          /* 16 */
+  int32_t num_blocks;          /* NB of the cache pools */
+  int32_t max_blocks_per_seq;  /* MB: block_tables row length */
+  int32_t dtype;               /* pa_dtype_t of q, k_new, v_new, caches and out */
+  int32_t max_query_len;       /* bound on L_b (<= 0: num_tokens) */
+} pa_prefill_dims_t;
+
+pa_status_t pa_prefill(const pa_prefill_dims_t* dims, void* out, const void* q,
+                       const void* k_new, const void* v_new, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start, float scale,
+                       void* stream);
+/* pa_prefill plus runtime timestamps (hipEvent_t, may be NULL) recorded around the
+ * kernel on the same stream. */
+pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const void* q,
+                                const void* k_new, const void* v_new, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, void* stream, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -38,6 +38,14 @@ class PaDims(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class PaPrefillDims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_query_len", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -70,6 +78,10 @@ SIGNATURES = {
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
     "pa_split_plan": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P]),
+    "pa_prefill": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          ctypes.c_float, _P]),
+    "pa_prefill_profiled": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _P, ctypes.c_float, _P, _P, _P]),
 }
 
 LAYOUT_FIELDS = 9
@@ -310,6 +322,47 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
                                 int(block_bytes), int(k_cache.shape[0]),
                                 ctypes.c_void_p(block_pairs.data_ptr()), int(block_pairs.shape[0]),
                                 _stream(stream)))
+
+
+def prefill_dims_of(q, k_new, k_cache, block_tables, context_lens, max_query_len=0):
+    """pa_prefill_dims_t from tensor shapes: q [T,Hq,D], k_new [T,Hkv,D], k_cache
+    [NB,Hkv,bs,D], block_tables [S,MB], context_lens [S]."""
+    if q.dim() != 3 or k_new.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise PaError(-3, "q / k_new must be 3-D, k_cache 4-D and block_tables 2-D")
+    T, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(k_new.shape) != (T, Hkv, D):
+        raise PaError(-3, "k_new must be [T, Hkv, D] matching q and k_cache")
+    return PaPrefillDims(context_lens.shape[0], T, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                         _dtype_code(q), int(max_query_len))
+
+
+def pa_prefill(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, query_start,
+               scale, max_query_len=0, stream=None, start_event=None, stop_event=None):
+    """Paged prefix-prefill attention (include/pa_decode.h, pa_prefill); all device tensors."""
+    d = prefill_dims_of(q, k_new, k_cache, block_tables, context_lens, max_query_len)
+    for name, t in (("out", out), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        if t.dtype != q.dtype:
+            raise PaError(-2, f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if tuple(out.shape) != tuple(q.shape) or tuple(v_new.shape) != tuple(k_new.shape) or \
+            tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise PaError(-3, "out / v_new / v_cache shapes must match q / k_new / k_cache")
+    if query_start.dim() != 1 or query_start.shape[0] != context_lens.shape[0] + 1 or \
+            block_tables.shape[0] != context_lens.shape[0]:
+        raise PaError(-3, "query_start needs S+1 entries, block_tables one row per sequence")
+    import torch
+    ptrs = (_ptr(out, "out"), _ptr(q, "q"), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+            _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+            _ptr(block_tables, "block_tables", torch.int32),
+            _ptr(context_lens, "context_lens", torch.int32),
+            _ptr(query_start, "query_start", torch.int32))
+    if start_event is None and stop_event is None:
+        _check(lib().pa_prefill(ctypes.byref(d), *ptrs, float(scale), _stream(stream)))
+    else:
+        _check(lib().pa_prefill_profiled(ctypes.byref(d), *ptrs, float(scale), _stream(stream),
+                                         start_event, stop_event))
+    return out
 
 
 def workspace_layout(q, k_cache, block_tables, max_context_len=0, partition_size=512):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libpa_decode.so"
-SOURCES = ["pa_api.hip", "pa_kernels.hip", "pa_copy.hip"]
+SOURCES = ["pa_api.hip", "pa_kernels.hip", "pa_copy.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 # hipcc flags.  Packed fp32 instructions are disabled for every HIP source.

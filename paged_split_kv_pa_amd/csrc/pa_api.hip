@@ -410,6 +410,73 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   return run_reduce(dims, pl, out, ctx, workspace, hs, sp);
 }
 
+pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, const void* kn,
+                         const void* vn, const void* kc, const void* vc, const int32_t* bt,
+                         const int32_t* ctx, const int32_t* qs, float scale, void* stream,
+                         hipEvent_t e0, hipEvent_t e1) {
+  if (!d) return fail(PA_ERR_NULL, "dims is NULL");
+  if (d->dtype != PA_F32 && d->dtype != PA_F16 && d->dtype != PA_BF16)
+    return fail(PA_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->num_seqs < 0 || d->num_tokens < 0)
+    return fail(PA_ERR_SHAPE, "num_seqs (%d) and num_tokens (%d) must be non-negative",
+                d->num_seqs, d->num_tokens);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->head_dim <= 0 ||
+      d->block_size <= 0)
+    return fail(PA_ERR_SHAPE, "num_blocks, max_blocks_per_seq, head_dim and block_size must be "
+                "positive");
+  if (d->max_query_len > d->num_tokens)
+    return fail(PA_ERR_SHAPE, "max_query_len %d exceeds num_tokens %d", d->max_query_len,
+                d->num_tokens);
+  if (d->dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "prefill is built for fp16 and bf16 (matrix cores)");
+  if (d->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)", d->head_dim);
+  if (d->block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", d->block_size);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8, 16)", G);
+  if ((int64_t)d->max_blocks_per_seq * pa::kBlockSize > (int64_t)0x3fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq %d exceeds the 2^30-token limit",
+                d->max_blocks_per_seq);
+  if (d->num_kv_heads > 65535 || d->num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads and num_seqs must be <= 65535 (grid limits)");
+  pa_status_t st = check_scale(scale);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0 || d->num_tokens == 0) return ok();
+  if (!out || !q || !kn || !vn || !kc || !vc || !bt || !ctx || !qs)
+    return fail(PA_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kn) || !aligned16(vn) || !aligned16(kc) ||
+      !aligned16(vc))
+    return fail(PA_ERR_ALIGN, "out, q, k_new, v_new and the caches must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(bt) | reinterpret_cast<uintptr_t>(ctx) |
+       reinterpret_cast<uintptr_t>(qs)) & 3u)
+    return fail(PA_ERR_ALIGN, "block_tables, context_lens and query_start must be 4-byte aligned");
+  const int maxq = d->max_query_len > 0 ? d->max_query_len : d->num_tokens;
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_new = kn;
+  a.v_new = vn;
+  a.k_cache = kc;
+  a.v_cache = vc;
+  a.bt = bt;
+  a.ctx = ctx;
+  a.query_start = qs;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.T = d->num_tokens;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.NB = d->num_blocks;
+  a.MB = d->max_blocks_per_seq;
+  return hip_status(pa::launch_prefill(d->dtype, G, a, d->num_seqs, maxq,
+                                       static_cast<hipStream_t>(stream), e0, e1),
+                    "prefill launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -608,6 +675,33 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, in
     return hip_status(pa::launch_copy_blocks(a, num_pairs, v_cache != nullptr,
                                              static_cast<hipStream_t>(stream)),
                       "block-copy launch");
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_prefill(const pa_prefill_dims_t* dims, void* out, const void* q,
+                       const void* k_new, const void* v_new, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start, float scale,
+                       void* stream) {
+  try {
+    return prefill_impl(dims, out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                        context_lens, query_start, scale, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const void* q,
+                                const void* k_new, const void* v_new, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                float scale, void* stream, void* start_event, void* stop_event) {
+  try {
+    return prefill_impl(dims, out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                        context_lens, query_start, scale, stream,
+                        static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }

@@ -1,0 +1,318 @@
+// Paged prefix-prefill attention for gfx950 (MI355X).
+//
+// Source: project_6 optimizations/prefix_prefill_patch.py (commit fee8f1b), docstring:
+// the prefix_prefill kernel is Flash-Attention style -- a grid of (batch, heads,
+// query tiles of BLOCK_M positions), K/V tiles of BLOCK_N tokens staged in on-chip
+// memory, fp16/bf16, head_dim 128, GQA.  What it computes (the reading stated with the
+// oracle): new token i of sequence b (absolute position c_b + i) attends to the c_b
+// prefix tokens in the paged cache and to new tokens 0..i, whose K/V arrive packed.
+//
+// Work-group: 4 waves, 256 query rows of one KV head g of one sequence: positions
+// [p0, p0 + 256/G) x the G query heads of g, row r = (position p0 + r / G, head
+// g*G + r % G).  Sharing every K/V tile among the G heads and 256/G positions is what
+// makes the tile traffic small next to the MFMA work.  Wave w owns rows 64w..64w+63,
+// as four column groups of 16 rows (the MFMA's 16 columns).
+//
+// Per 64-key tile: K and V rows are loaded from the cache (key < c, through the
+// block table) or from the packed new tokens (c <= key < c + L), into LDS rows of
+// 256 bytes whose 16-byte chunks are XOR-swizzled with the row index, so that both
+// operand reads below hit 16 distinct chunk positions per 16 lanes.
+//   S^T = K Q^T:   v_mfma_f32_16x16x32, A = 16 keys x 32 dims (LDS), B = Q (registers):
+//                  lane (r16, kg) gets keys 4kg..4kg+3 of query row r16.
+//   online softmax per query row in base 2 (scale * log2 e folded in), causal mask on
+//                  the tiles that reach the row's own position, lazy rescale as in decode.
+//   O += P V:      v_mfma_f32_16x16x32 over 32 keys = two 16-key row blocks: the S^T
+//                  accumulators of the two blocks are exactly the A operand (k-slot e of
+//                  lane group kg is key 16(2s + e/4) + 4kg + e%4), and the B operand
+//                  takes column j of the 16-byte V runs of those 8 keys (v_perm pairs),
+//                  so instruction j produces head-dim indices 8n + j.
+// The next tile's global loads are issued before the current tile's math.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_decode.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.f;
+constexpr int kD = 128;          // head_dim built
+constexpr int kRows = 256;       // query rows per work-group
+constexpr int kTile = 64;        // keys per K/V tile
+constexpr int kChunks = kD / 8;  // 16-byte chunks per row
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  uint16_t l, h;
+  if constexpr (BF) {
+    l = __builtin_bit_cast(uint16_t, (__bf16)lo);
+    h = __builtin_bit_cast(uint16_t, (__bf16)hi);
+  } else {
+    l = __builtin_bit_cast(uint16_t, (_Float16)lo);
+    h = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  }
+  return (uint32_t)l | ((uint32_t)h << 16);
+}
+
+// LDS slot (in 16-byte units) of chunk `c` of tile row `r`.
+__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 15)); }
+
+template <int DT, int G>
+__global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
+  constexpr bool kBF = DT == PA_BF16;
+  constexpr int kPos = kRows / G;  // query positions per work-group
+  __shared__ u32x4 s_k[kTile * kChunks];
+  __shared__ u32x4 s_v[kTile * kChunks];
+
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int p0 = blockIdx.x * kPos;
+  int r1 = a.query_start[b + 1], r0 = a.query_start[b];
+  r1 = min(r1, a.T);
+  r0 = min(max(r0, 0), r1);
+  const int L = r1 - r0;
+  if (p0 >= L) return;
+  int c = a.ctx[b];
+  const int cap = a.MB * kBlockSize;
+  c = c < 0 ? 0 : (c > cap ? cap : c);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  // Keys this work-group needs: the prefix and new tokens up to its last position.
+  const int pend = min(L, p0 + kPos);
+  const int nkeys = c + pend;
+  const int ntiles = (nkeys + kTile - 1) / kTile;
+
+  // ---- query operands and per-row state ----
+  // Column group cg of this wave: rows 64w + 16cg + (0..15); lane column r16.
+  u32x4 qf[4][4];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
+  int qpos_col[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    const int row = 64 * w + 16 * cg + r16;
+    const int pos = p0 + row / G;
+    const int hq = g * G + row % G;
+    qpos_col[cg] = pos;
+    const bool valid = pos < L;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[cg][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
+                         : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x4 O[4][8];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[4], l_run[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    m_ref[cg] = kNegInf;
+    l_run[cg] = 0.f;
+  }
+
+  // ---- tile loads: thread tid moves 64 bytes (4 chunks) of K and of V of tile row tid/4 ----
+  const int lrow = tid >> 2, lc0 = (tid & 3) * 4;
+  const size_t hstride = (size_t)kBlockSize * kD;  // elements per (block, head)
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
+  const size_t bstride = (size_t)a.Hkv * hstride;
+  u32x4 kr[4], vr[4];
+  auto load_tile = [&](int t) {
+    const int key = t * kTile + lrow;
+    const uint16_t* ks = nullptr;
+    const uint16_t* vs = nullptr;
+    if (key < c) {
+      const int blk = a.bt[(size_t)b * a.MB + key / kBlockSize];
+      if ((unsigned)blk < (unsigned)a.NB) {
+        const size_t off = (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD;
+        ks = kc + off;
+        vs = vc + off;
+      }
+    } else if (key < nkeys) {
+      const size_t off = ((size_t)(r0 + key - c) * a.Hkv + g) * kD;
+      ks = static_cast<const uint16_t*>(a.k_new) + off;
+      vs = static_cast<const uint16_t*>(a.v_new) + off;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = ks ? *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i)) : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = vs ? *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  load_tile(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_k[swz(lrow, lc0 + i)] = kr[i];
+      s_v[swz(lrow, lc0 + i)] = vr[i];
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
+
+    // S^T = K Q^T for 4 row blocks of 16 keys x 4 column groups.
+    f32x4 S[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 ka = s_k[swz(16 * rb + r16, 4 * kk + kg)];
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) S[rb][cg] = mfma32<kBF>(ka, qf[cg][kk], S[rb][cg]);
+      }
+    }
+
+    // Online softmax per column group; P packed as the A operand of the PV products.
+    const int kbase = t * kTile;
+    const bool diag = kbase + kTile - 1 > c + p0;  // some key may lie after some row
+    u32x4 Pa[4][2];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      float x[4][4];
+      const int lim = c + qpos_col[cg];  // last visible key of query row r16
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + 16 * rb + 4 * kg + i;
+          const bool vis = !diag || (key <= lim && key < nkeys);
+          x[rb][i] = vis ? S[rb][cg][i] * a.scale_log2 : kNegInf;
+        }
+      float bm = kNegInf;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        bm = fmaxf(bm, fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      if (__any(bm > m_ref[cg] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref[cg], bm);
+        const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
+        l_run[cg] *= alpha;
+        m_ref[cg] = m_new;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+      }
+      float p[4][4];
+      float ls = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[rb][i] = x[rb][i] == kNegInf ? 0.f : exp2_fast(x[rb][i] - m_ref[cg]);
+          ls += p[rb][i];
+        }
+      l_run[cg] += ls;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        Pa[cg][s] = u32x4{pack2<kBF>(p[2 * s][0], p[2 * s][1]), pack2<kBF>(p[2 * s][2], p[2 * s][3]),
+                          pack2<kBF>(p[2 * s + 1][0], p[2 * s + 1][1]),
+                          pack2<kBF>(p[2 * s + 1][2], p[2 * s + 1][3])};
+    }
+
+    // O += P V over two 32-key steps.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 run[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg][s], bv, O[cg][j]);
+      }
+    }
+  }
+
+  // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 8 r16 .. +7 ----
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    float l = l_run[cg];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(l, 4 * kg + i);
+      const int row = 64 * w + 16 * cg + 4 * kg + i;
+      const int pos = p0 + row / G;
+      if (pos >= L) continue;
+      const int hq = g * G + row % G;
+      const float inv = 1.f / li;
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * kD;
+      *reinterpret_cast<u32x4*>(orow + 8 * r16) =
+          u32x4{pack2<kBF>(O[cg][0][i] * inv, O[cg][1][i] * inv),
+                pack2<kBF>(O[cg][2][i] * inv, O[cg][3][i] * inv),
+                pack2<kBF>(O[cg][4][i] * inv, O[cg][5][i] * inv),
+                pack2<kBF>(O[cg][6][i] * inv, O[cg][7][i] * inv)};
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<DT, 8>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<DT, 16>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_positions_per_workgroup(int group) { return kRows / group; }
+
+hipError_t launch_prefill(int dtype, int group, const PrefillArgs& a, int num_seqs,
+                          int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const int per = kRows / group;
+  const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
+  if (e0) (void)hipEventRecord(e0, stream);
+  hipError_t err = dtype == PA_BF16 ? launch_g<PA_BF16>(group, a, grid, stream)
+                 : dtype == PA_F16  ? launch_g<PA_F16>(group, a, grid, stream)
+                                    : hipErrorInvalidValue;
+  if (e1) (void)hipEventRecord(e1, stream);
+  return err;
+}
+
+}  // namespace pa

@@ -359,3 +359,51 @@ def test_copy_blocks_validation():
     assert lib.pa_copy_blocks(K, ctypes.c_void_p(0x10008), 4096, 10, PR, 1, None) == -4
     assert lib.pa_copy_blocks(K, V, 4096, 10, ctypes.c_void_p(0x10002), 1, None) == -4
     assert "block_pairs" in B.pa_last_error()
+
+
+def pdims(**kw):
+    d = dict(num_seqs=2, num_tokens=100, num_q_heads=32, num_kv_heads=4, head_dim=128,
+             block_size=16, num_blocks=64, max_blocks_per_seq=8, dtype=B.PA_BF16,
+             max_query_len=0)
+    d.update(kw)
+    return B.PaPrefillDims(**d)
+
+
+PF_FAKE = [ctypes.c_void_p(0x20000 + 0x1000 * i) for i in range(9)]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), -2),
+    (dict(num_seqs=-1), -3),
+    (dict(num_tokens=-1), -3),
+    (dict(num_q_heads=30), -3),
+    (dict(num_blocks=0), -3),
+    (dict(max_query_len=101), -3),
+    (dict(dtype=B.PA_F32), -6),
+    (dict(head_dim=256), -6),
+    (dict(block_size=32), -6),
+    (dict(num_q_heads=96, num_kv_heads=4), -6),   # G = 24
+    (dict(num_kv_heads=70000, num_q_heads=70000), -6),
+])
+def test_prefill_validation(kw, status):
+    st = B.lib().pa_prefill(ctypes.byref(pdims(**kw)), *PF_FAKE, 0.1, None)
+    assert st == status, B.pa_last_error()
+
+
+def test_prefill_pointers_and_empty_calls():
+    lib = B.lib()
+    assert lib.pa_prefill(None, *PF_FAKE, 0.1, None) == -1
+    for i in range(9):
+        ptrs = list(PF_FAKE)
+        ptrs[i] = ctypes.c_void_p(0)
+        assert lib.pa_prefill(ctypes.byref(pdims()), *ptrs, 0.1, None) == -1
+    ptrs = list(PF_FAKE)
+    ptrs[1] = ctypes.c_void_p(0x20008)  # q misaligned
+    assert lib.pa_prefill(ctypes.byref(pdims()), *ptrs, 0.1, None) == -4
+    ptrs = list(PF_FAKE)
+    ptrs[8] = ctypes.c_void_p(0x20002)  # query_start misaligned
+    assert lib.pa_prefill(ctypes.byref(pdims()), *ptrs, 0.1, None) == -4
+    assert lib.pa_prefill(ctypes.byref(pdims()), *PF_FAKE, float("nan"), None) == -3
+    nul = [ctypes.c_void_p(0)] * 9
+    assert lib.pa_prefill(ctypes.byref(pdims(num_tokens=0)), *nul, 0.1, None) == 0
+    assert lib.pa_prefill(ctypes.byref(pdims(num_seqs=0)), *nul, 0.1, None) == 0
