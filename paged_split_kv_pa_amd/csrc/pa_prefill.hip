@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "pa_decode.h"
 #include "pa_internal.h"
 
@@ -124,6 +125,17 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       qf[cg][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
                          : u32x4{0u, 0u, 0u, 0u};
   }
+  // The softmax works on raw dot products scaled by |scale| log2(e); a negative scale is
+  // carried by flipping the sign of q (exact in 16-bit floats), so max(scale * s) is
+  // |scale| * max of the flipped products.
+  const float sl = fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.f) {
+    const uint32_t flip = 0x80008000u;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[cg][kk] ^= u32x4{flip, flip, flip, flip};
+  }
   f32x4 O[4][8];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg)
@@ -137,127 +149,154 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
   }
 
   // ---- tile loads: thread tid moves 64 bytes (4 chunks) of K and of V of tile row tid/4 ----
+  // Loads are unconditional (a row outside the keys reads a valid dummy row and is
+  // zeroed when written to LDS), so no branch or wait sits between them.  The block id
+  // of a prefix row is read two tiles ahead, behind the K/V loads of the next tile:
+  // consuming it never drains loads that are still useful in flight.
   const int lrow = tid >> 2, lc0 = (tid & 3) * 4;
   const size_t hstride = (size_t)kBlockSize * kD;  // elements per (block, head)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
+  const uint16_t* knew = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vnew = static_cast<const uint16_t*>(a.v_new);
   const size_t bstride = (size_t)a.Hkv * hstride;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB;
+  const int cmax = c > 0 ? c - 1 : 0;
+  auto fetch_block = [&](int t) {  // block id of this thread's row of tile t (any if not prefix)
+    return btrow[min(t * kTile + lrow, cmax) / kBlockSize];
+  };
   u32x4 kr[4], vr[4];
-  auto load_tile = [&](int t) {
+  bool row_ok = false;
+  auto load_tile = [&](int t, int blk) {
     const int key = t * kTile + lrow;
-    const uint16_t* ks = nullptr;
-    const uint16_t* vs = nullptr;
-    if (key < c) {
-      const int blk = a.bt[(size_t)b * a.MB + key / kBlockSize];
-      if ((unsigned)blk < (unsigned)a.NB) {
-        const size_t off = (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD;
-        ks = kc + off;
-        vs = vc + off;
-      }
-    } else if (key < nkeys) {
-      const size_t off = ((size_t)(r0 + key - c) * a.Hkv + g) * kD;
-      ks = static_cast<const uint16_t*>(a.k_new) + off;
-      vs = static_cast<const uint16_t*>(a.v_new) + off;
-    }
+    const bool pre = key < c && (unsigned)blk < (unsigned)a.NB;
+    const bool fresh = key >= c && key < nkeys;
+    row_ok = pre || fresh;
+    const size_t off = pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD
+                           : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * kD : (size_t)r0 * a.Hkv * kD);
+    const uint16_t* ks = (pre ? kc : knew) + off;
+    const uint16_t* vs = (pre ? vc : vnew) + off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kr[i] = ks ? *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i)) : u32x4{0u, 0u, 0u, 0u};
-      vr[i] = vs ? *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i)) : u32x4{0u, 0u, 0u, 0u};
+      kr[i] = *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i));
+      vr[i] = *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i));
     }
   };
 
-  load_tile(0);
+  int blk_next = fetch_block(1);
+  load_tile(0, fetch_block(0));
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();  // the previous tile's LDS reads are done
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s_k[swz(lrow, lc0 + i)] = kr[i];
-      s_v[swz(lrow, lc0 + i)] = vr[i];
+      s_k[swz(lrow, lc0 + i)] = row_ok ? kr[i] : z;
+      s_v[swz(lrow, lc0 + i)] = row_ok ? vr[i] : z;
     }
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
-
-    // S^T = K Q^T for 4 row blocks of 16 keys x 4 column groups.
-    f32x4 S[4][4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 ka = s_k[swz(16 * rb + r16, 4 * kk + kg)];
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) S[rb][cg] = mfma32<kBF>(ka, qf[cg][kk], S[rb][cg]);
-      }
+    if (t + 1 < ntiles) {  // in flight during this tile's math
+      load_tile(t + 1, blk_next);
+      blk_next = fetch_block(t + 2);
     }
 
-    // Online softmax per column group; P packed as the A operand of the PV products.
+    // Two 32-key steps per tile (two 16-key row blocks each): S^T, softmax and O += P V
+    // per step keep the live accumulators small enough for the operand reads to be
+    // batched instead of serialised.
     const int kbase = t * kTile;
-    const bool diag = kbase + kTile - 1 > c + p0;  // some key may lie after some row
-    u32x4 Pa[4][2];
+    const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
+    {
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      float x[4][4];
-      const int lim = c + qpos_col[cg];  // last visible key of query row r16
+      for (int s = 0; s < 2; ++s) {
+        // S^T = K Q^T for row blocks 2s, 2s+1 x 4 column groups.
+        u32x4 ka[2][4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + 16 * rb + 4 * kg + i;
-          const bool vis = !diag || (key <= lim && key < nkeys);
-          x[rb][i] = vis ? S[rb][cg][i] * a.scale_log2 : kNegInf;
-        }
-      float bm = kNegInf;
+          for (int kk = 0; kk < 4; ++kk)
+            ka[h][kk] = s_k[swz(16 * (2 * s + h) + r16, 4 * kk + kg)];
+        f32x4 S[2][4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        bm = fmaxf(bm, fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      if (__any(bm > m_ref[cg] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_ref[cg], bm);
-        const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
-        l_run[cg] *= alpha;
-        m_ref[cg] = m_new;
-        float al[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+          for (int cg = 0; cg < 4; ++cg) {
+            S[h][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
-      }
-      float p[4][4];
-      float ls = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[rb][i] = x[rb][i] == kNegInf ? 0.f : exp2_fast(x[rb][i] - m_ref[cg]);
-          ls += p[rb][i];
-        }
-      l_run[cg] += ls;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        Pa[cg][s] = u32x4{pack2<kBF>(p[2 * s][0], p[2 * s][1]), pack2<kBF>(p[2 * s][2], p[2 * s][3]),
-                          pack2<kBF>(p[2 * s + 1][0], p[2 * s + 1][1]),
-                          pack2<kBF>(p[2 * s + 1][2], p[2 * s + 1][3])};
-    }
+            for (int kk = 0; kk < 4; ++kk)
+              S[h][cg] = mfma32<kBF>(ka[h][kk], qf[cg][kk], S[h][cg]);
+          }
 
-    // O += P V over two 32-key steps.
+        // Online softmax per column group; P packed as the A operand of the PV product
+        // (k-slot e of lane group kg is key 16(2s + e/4) + 4kg + e%4).
+        u32x4 Pa[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 run[8];
+        for (int cg = 0; cg < 4; ++cg) {
+          // S becomes the base-2 logit; on the tiles that reach past the work-group's
+          // first position, -inf where the key is masked (exp2 of -inf - m is 0).
+          if (diag) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+              for (int i = 0; i < 4; ++i) {
+                const int key = kbase + 16 * (2 * s + h) + 4 * kg + i;
+                const bool vis = key <= c + qpos_col[cg] && key < nkeys;
+                S[h][cg][i] = vis ? S[h][cg][i] * sl : kNegInf;
+              }
+          } else {
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg][s], bv, O[cg][j]);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) S[h][cg][i] *= sl;
+          }
+          float bm = kNegInf;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bm = fmaxf(bm, fmaxf(fmaxf(S[h][cg][0], S[h][cg][1]), fmaxf(S[h][cg][2], S[h][cg][3])));
+          bm = fmaxf(bm, __shfl_xor(bm, 16));
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          if (__any(bm > m_ref[cg] + kRescaleSlack)) {
+            const float m_new = fmaxf(m_ref[cg], bm);
+            const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
+            l_run[cg] *= alpha;
+            m_ref[cg] = m_new;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+          }
+          // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
+          const float nm = -m_ref[cg];
+          float p[2][4];
+          float ls = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              p[h][i] = exp2_fast(S[h][cg][i] + nm);
+              ls += p[h][i];
+            }
+          l_run[cg] += ls;
+          Pa[cg] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
+                         pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+        }
+
+        // O += P V over these 32 keys.
+        u32x4 run[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+#pragma unroll
+          for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg], bv, O[cg][j]);
+        }
       }
     }
   }
