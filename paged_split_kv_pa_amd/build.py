@@ -27,6 +27,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags.  The prefill kernel keeps its 128 output accumulators per lane in
+# VGPRs (the softmax rescales them with VALU instructions); in the default AGPR form the
+# compiler copied them between the register files on every K/V tile.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -58,7 +64,8 @@ def build(verbose=False, extra_flags=()):
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *HIPCC_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     out = os.path.join(LIBDIR, LIBNAME)

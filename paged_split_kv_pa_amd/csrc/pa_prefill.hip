@@ -136,17 +136,32 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qf[cg][kk] ^= u32x4{flip, flip, flip, flip};
   }
+  // Register classes, pinned with empty asm constraints: the output and score
+  // accumulators live in VGPRs (the softmax and the rare rescale work on them there),
+  // while MFMA input operands (queries, K rows) and the staged tile loads live in AGPRs.
+  // Left to itself the compiler kept the output accumulators in AGPRs and copied all
+  // 128 of them to VGPRs and back on every tile.
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) asm("" : "+a"(qf[cg][kk]));
   f32x4 O[4][8];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
     for (int j = 0; j < 8; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[4], l_run[4];
+  // Row sums of P come from the matrix cores too: one more PV product per column group
+  // with an all-ones B operand leaves sum_k P[row][k] in every column, in the same
+  // row layout as O (and from the same bf16-rounded P as O).
+  f32x4 Lacc[4];
+  float m_ref[4];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) {
     m_ref[cg] = kNegInf;
-    l_run[cg] = 0.f;
+    Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const uint32_t one2 = kBF ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0
+  const u32x4 ones = {one2, one2, one2, one2};
 
   // ---- tile loads: thread tid moves 64 bytes (4 chunks) of K and of V of tile row tid/4 ----
   // Loads are unconditional (a row outside the keys reads a valid dummy row and is
@@ -180,6 +195,8 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
     for (int i = 0; i < 4; ++i) {
       kr[i] = *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i));
       vr[i] = *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i));
+      asm("" : "+a"(kr[i]));
+      asm("" : "+a"(vr[i]));
     }
   };
 
@@ -212,8 +229,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < 4; ++kk) {
             ka[h][kk] = s_k[swz(16 * (2 * s + h) + r16, 4 * kk + kg)];
+            asm("" : "+a"(ka[h][kk]));
+          }
         f32x4 S[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -223,6 +242,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
               S[h][cg] = mfma32<kBF>(ka[h][kk], qf[cg][kk], S[h][cg]);
+            asm("" : "+v"(S[h][cg]));
           }
 
         // Online softmax per column group; P packed as the A operand of the PV product
@@ -230,8 +250,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
         u32x4 Pa[4];
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
-          // S becomes the base-2 logit; on the tiles that reach past the work-group's
-          // first position, -inf where the key is masked (exp2 of -inf - m is 0).
+          // On the tiles that reach past the work-group's first position, S becomes the
+          // base-2 logit with -inf where the key is masked (exp2 of -inf - m is 0);
+          // elsewhere the max of the raw products is scaled once and p is one fused
+          // multiply-add and an exp2.
           if (diag) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -241,11 +263,6 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
                 const bool vis = key <= c + qpos_col[cg] && key < nkeys;
                 S[h][cg][i] = vis ? S[h][cg][i] * sl : kNegInf;
               }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) S[h][cg][i] *= sl;
           }
           float bm = kNegInf;
 #pragma unroll
@@ -253,10 +270,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
             bm = fmaxf(bm, fmaxf(fmaxf(S[h][cg][0], S[h][cg][1]), fmaxf(S[h][cg][2], S[h][cg][3])));
           bm = fmaxf(bm, __shfl_xor(bm, 16));
           bm = fmaxf(bm, __shfl_xor(bm, 32));
+          if (!diag) bm *= sl;  // base-2 max of the row over these keys
           if (__any(bm > m_ref[cg] + kRescaleSlack)) {
             const float m_new = fmaxf(m_ref[cg], bm);
             const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
-            l_run[cg] *= alpha;
             m_ref[cg] = m_new;
             float al[4];
 #pragma unroll
@@ -265,19 +282,17 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
             for (int j = 0; j < 8; ++j)
 #pragma unroll
               for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
           }
           // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
           const float nm = -m_ref[cg];
+          const float fs = diag ? 1.f : sl;  // masked tiles hold scaled logits already
           float p[2][4];
-          float ls = 0.f;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              p[h][i] = exp2_fast(S[h][cg][i] + nm);
-              ls += p[h][i];
-            }
-          l_run[cg] += ls;
+            for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[h][cg][i], fs, nm));
           Pa[cg] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
                          pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
         }
@@ -297,19 +312,22 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg], bv, O[cg][j]);
         }
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) Lacc[cg] = mfma32<kBF>(Pa[cg], ones, Lacc[cg]);
       }
     }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm("" : "+v"(O[cg][j]));
   }
 
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 8 r16 .. +7 ----
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) {
-    float l = l_run[cg];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(l, 4 * kg + i);
+      const float li = Lacc[cg][i];
       const int row = 64 * w + 16 * cg + 4 * kg + i;
       const int pos = p0 + row / G;
       if (pos >= L) continue;
