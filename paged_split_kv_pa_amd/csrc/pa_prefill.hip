@@ -216,106 +216,124 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       blk_next = fetch_block(t + 2);
     }
 
-    // Two 32-key steps per tile (two 16-key row blocks each): S^T, softmax and O += P V
-    // per step keep the live accumulators small enough for the operand reads to be
-    // batched instead of serialised.
+    // Per tile: S^T for both 32-key halves (matrix cores), the row maxima over the 64
+    // keys and one rescale decision (VALU), then P and O += P V per half.  The PV
+    // products of the first half are interleaved with the exponentials of the second
+    // (scheduling groups), so the matrix cores and the VALU work at the same time.
     const int kbase = t * kTile;
     const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
-    {
+    f32x4 S[2][2][4];  // [half][row block][column group]
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        // S^T = K Q^T for row blocks 2s, 2s+1 x 4 column groups.
-        u32x4 ka[2][4];
+    for (int s = 0; s < 2; ++s) {
+      u32x4 ka[2][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            ka[h][kk] = s_k[swz(16 * (2 * s + h) + r16, 4 * kk + kg)];
-            asm("" : "+a"(ka[h][kk]));
-          }
-        f32x4 S[2][4];
+        for (int kk = 0; kk < 4; ++kk) {
+          ka[h][kk] = s_k[swz(16 * (2 * s + h) + r16, 4 * kk + kg)];
+          asm("" : "+a"(ka[h][kk]));
+        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int cg = 0; cg < 4; ++cg) {
-            S[h][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              S[h][cg] = mfma32<kBF>(ka[h][kk], qf[cg][kk], S[h][cg]);
-            asm("" : "+v"(S[h][cg]));
-          }
-
-        // Online softmax per column group; P packed as the A operand of the PV product
-        // (k-slot e of lane group kg is key 16(2s + e/4) + 4kg + e%4).
-        u32x4 Pa[4];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
-          // On the tiles that reach past the work-group's first position, S becomes the
-          // base-2 logit with -inf where the key is masked (exp2 of -inf - m is 0);
-          // elsewhere the max of the raw products is scaled once and p is one fused
-          // multiply-add and an exp2.
+          S[s][h][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            S[s][h][cg] = mfma32<kBF>(ka[h][kk], qf[cg][kk], S[s][h][cg]);
+        }
+    }
+
+    // Row maxima (base 2) over the tile; masked keys become -inf on diagonal tiles,
+    // where S then holds scaled logits (exp2 of -inf - m is 0).
+    float bm[4];
+    bool grow = false;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
           if (diag) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = kbase + 16 * (2 * s + h) + 4 * kg + i;
-                const bool vis = key <= c + qpos_col[cg] && key < nkeys;
-                S[h][cg][i] = vis ? S[h][cg][i] * sl : kNegInf;
-              }
+            for (int i = 0; i < 4; ++i) {
+              const int key = kbase + 16 * (2 * s + h) + 4 * kg + i;
+              const bool vis = key <= c + qpos_col[cg] && key < nkeys;
+              S[s][h][cg][i] = vis ? S[s][h][cg][i] * sl : kNegInf;
+            }
           }
-          float bm = kNegInf;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            bm = fmaxf(bm, fmaxf(fmaxf(S[h][cg][0], S[h][cg][1]), fmaxf(S[h][cg][2], S[h][cg][3])));
-          bm = fmaxf(bm, __shfl_xor(bm, 16));
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
-          if (!diag) bm *= sl;  // base-2 max of the row over these keys
-          if (__any(bm > m_ref[cg] + kRescaleSlack)) {
-            const float m_new = fmaxf(m_ref[cg], bm);
-            const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
-            m_ref[cg] = m_new;
-            float al[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
-          }
-          // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
-          const float nm = -m_ref[cg];
-          const float fs = diag ? 1.f : sl;  // masked tiles hold scaled logits already
-          float p[2][4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[h][cg][i], fs, nm));
-          Pa[cg] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
-                         pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+          mx = fmaxf(mx, fmaxf(fmaxf(S[s][h][cg][0], S[s][h][cg][1]),
+                               fmaxf(S[s][h][cg][2], S[s][h][cg][3])));
         }
-
-        // O += P V over these 32 keys.
-        u32x4 run[8];
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      bm[cg] = diag ? mx : mx * sl;
+      grow = grow || bm[cg] > m_ref[cg] + kRescaleSlack;
+    }
+    if (__any(grow)) {  // rare: one branch per tile for all column groups
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+      for (int cg = 0; cg < 4; ++cg) {
+        const float m_new = fmaxf(m_ref[cg], bm[cg]);
+        const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
+        m_ref[cg] = m_new;
+        float al[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-          const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
 #pragma unroll
-          for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg], bv, O[cg][j]);
-        }
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) Lacc[cg] = mfma32<kBF>(Pa[cg], ones, Lacc[cg]);
+          for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
       }
     }
+
+    // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
+    const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
+    auto probs = [&](int s, u32x4 (&Pa)[4]) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        const float nm = -m_ref[cg];
+        float p[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[s][h][cg][i], fs, nm));
+        Pa[cg] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
+                       pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+      }
+    };
+    auto pv = [&](int s, const u32x4 (&Pa)[4]) {
+      u32x4 run[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
+                               __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg], bv, O[cg][j]);
+      }
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) Lacc[cg] = mfma32<kBF>(Pa[cg], ones, Lacc[cg]);
+    };
+    u32x4 P0[4], P1[4];
+    probs(0, P0);
+    pv(0, P0);
+    probs(1, P1);
+    // Interleave: each of PV(0)'s 36 products followed by up to 3 VALU instructions of
+    // the second half's exponentials and packing.
+#pragma unroll
+    for (int k = 0; k < 36; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three VALU
+    }
+    pv(1, P1);
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
