@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+MFMA_PEAK_TFLOPS_16BIT = 2500.0  # MI355X dense bf16 / fp16 matrix-core peak
 KERNEL_SOURCE = os.path.join(ROOT, "paged_split_kv_pa_amd", "csrc", "pa_kernels.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_long_100k_hbm_traffic.md")
 
@@ -74,8 +75,11 @@ def parse():
     ap.add_argument("--sweep-paths", action="store_true",
                     help="time forced V1 against forced V2 over a grid of batch sizes and "
                          "context lengths (32/4 heads, head_dim 128, bf16) and exit")
-    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
-                    help="decode (the headline) or the prefix-caching KV block copy")
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
+                    help="decode (the headline), the prefix-caching KV block copy, or paged "
+                         "prefix-prefill attention")
+    ap.add_argument("--prefill-config", type=int, default=1,
+                    help="prefill: workload index (1 = 8192-token chunk after a 65536 prefix)")
     ap.add_argument("--pairs", type=int, default=2048,
                     help="copy_blocks: (src, dst) block pairs per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -207,14 +211,17 @@ def bench_copy_blocks(args):
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
     call_args = [[ctypes.c_void_p(ks[c].data_ptr()), ctypes.c_void_p(vs[c].data_ptr()),
-                  block_bytes, NB, ctypes.c_void_p(pairs.data_ptr()), n, sptr] for c in range(R)]
+                  block_bytes, NB, ctypes.c_void_p(pairs.data_ptr()), n, sptr, None, None]
+                 for c in range(R)]
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
 
-    def step(i):
-        st = lib.pa_copy_blocks(*call_args[i % R])
+    def step(i, e0=None, e1=None):
+        a = call_args[i % R]
+        a[7], a[8] = e0, e1
+        st = lib.pa_copy_blocks_profiled(*a)
         if st != 0:
             raise B.PaError(st, B.pa_last_error())
 
@@ -238,9 +245,7 @@ def bench_copy_blocks(args):
             e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
             hip.hipEventCreate(ctypes.byref(e0))
             hip.hipEventCreate(ctypes.byref(e1))
-            hip.hipEventRecord(e0, sptr)
-            step(i)
-            hip.hipEventRecord(e1, sptr)
+            step(i, e0, e1)
             evs.append((e0, e1))
         else:
             step(i)
@@ -270,7 +275,7 @@ def bench_copy_blocks(args):
     plain_us = (time.perf_counter() - t1) * 1e6 / 50
     del srcs, dst
     log(f"copy_blocks: {n} pairs, {algo_bytes / 1e6:.1f} MB moved per call; call {us:.2f} us; "
-        f"kernel (event pair) mean {kmean:.2f} us, median {np.median(ker):.2f}")
+        f"kernel mean {kmean:.2f} us, median {np.median(ker):.2f}")
     rec = {
         "metric": "KV block copy GB/s (bytes read + written) + us/call, prefix-caching copy",
         "value": round(algo_bytes / (us / 1e6) / 1e9, 2),
@@ -306,6 +311,150 @@ def bench_copy_blocks(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_prefill(args):
+    """Paged prefix-prefill attention (pa_prefill) on a seeded prefill workload; the
+    metric is algorithmic TFLOP/s (2 D FLOP for q.k and 2 D for p.v per visible
+    (query row, key) pair, per head) against the MI355X dense bf16/fp16 peak."""
+    import ctypes
+    import torch
+    import oracle
+    from paged_split_kv_pa_amd import binding as B
+    from paged_split_kv_pa_amd import workloads as wl
+
+    w = wl.prefill_config(args.prefill_config)
+    log(f"prefill workload {w.name}: S={w.num_seqs} T={w.num_tokens} prefix "
+        f"{list(map(int, w.context_lens))} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
+    dev = {n: to_dev(getattr(w, n), w.dtype) for n in ("q", "k_new", "v_new", "k_cache",
+                                                        "v_cache")}
+    for n in ("block_tables", "context_lens", "query_start"):
+        dev[n] = torch.from_numpy(np.ascontiguousarray(getattr(w, n), dtype=np.int32)).cuda()
+    out = torch.empty_like(dev["q"])
+    flops = oracle.prefill_flops(w.context_lens, w.query_start, w.num_q_heads, w.head_dim)
+    lib = B.lib()
+    d = B.prefill_dims_of(dev["q"], dev["k_new"], dev["k_cache"], dev["block_tables"],
+                          dev["context_lens"], w.max_query_len)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    call = [ctypes.byref(d), vp(out), vp(dev["q"]), vp(dev["k_new"]), vp(dev["v_new"]),
+            vp(dev["k_cache"]), vp(dev["v_cache"]), vp(dev["block_tables"]),
+            vp(dev["context_lens"]), vp(dev["query_start"]), ctypes.c_float(w.scale), sptr,
+            None, None]
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+
+    def step(e0=None, e1=None):
+        call[12], call[13] = e0, e1
+        st = lib.pa_prefill_profiled(*call)
+        if st != 0:
+            raise B.PaError(st, B.pa_last_error())
+
+    step()
+    torch.cuda.synchronize()
+    # parity on sampled rows (the oracle computes single causal rows cheaply)
+    from oracle.storage import upcast
+    got = out.to(torch.float64).cpu().numpy()
+    rng = np.random.default_rng(1)
+    G = w.num_q_heads // w.num_kv_heads
+    worst = 0.0
+    s32 = float(np.float32(w.scale))
+    for _ in range(16):
+        b = int(rng.integers(0, w.num_seqs))
+        r0, r1 = int(w.query_start[b]), int(w.query_start[b + 1])
+        if r1 == r0:
+            continue
+        i = int(rng.integers(0, r1 - r0))
+        h = int(rng.integers(0, w.num_q_heads))
+        c = int(w.context_lens[b])
+        kp = upcast(oracle.gather_sequence(w.k_cache, w.block_tables, b, c), w.dtype)[:, h // G]
+        vp_ = upcast(oracle.gather_sequence(w.v_cache, w.block_tables, b, c), w.dtype)[:, h // G]
+        ka = np.concatenate([kp, upcast(w.k_new[r0:r0 + i + 1, h // G], w.dtype)])
+        va = np.concatenate([vp_, upcast(w.v_new[r0:r0 + i + 1, h // G], w.dtype)])
+        ref = oracle.prefill_rows(upcast(w.q[r0 + i:r0 + i + 1, h], w.dtype), ka, va, c + i,
+                                  s32)[0]
+        worst = max(worst, float(np.max(np.abs(got[r0 + i, h] - ref) / (2e-3 + 1e-2 * np.abs(ref)))))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i % max(1, args.event_every) == 0:
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(e0))
+            hip.hipEventCreate(ctypes.byref(e1))
+            step(e0, e1)
+            evs.append((e0, e1))
+        else:
+            step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ctypes.c_float()
+    ker = []
+    for e0, e1 in evs:
+        hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1)
+        ker.append(ms.value * 1e3)
+        hip.hipEventDestroy(e0)
+        hip.hipEventDestroy(e1)
+    us = wall * 1e6 / args.steps
+    kmean = float(np.mean(ker))
+    log(f"prefill: {flops / 1e12:.3f} TFLOP per call; call {us / 1e3:.3f} ms; kernel mean "
+        f"{kmean / 1e3:.3f} ms")
+    peak = MFMA_PEAK_TFLOPS_16BIT
+    rec = {
+        "metric": "prefix-prefill attention TFLOP/s (algorithmic, causal) + ms/call",
+        "value": round(flops / (us / 1e6) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_tokens": w.num_tokens,
+                   "context_lens": [int(x) for x in w.context_lens],
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": 16, "flops_per_call": flops},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kmean / 1e6) / 1e12, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / (kmean / 1e6) / 1e12 / peak, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "kernel_mean_us": round(kmean, 3),
+                     "kernel_samples": len(ker)},
+        "parity": {"sampled_rows": 16, "worst_tolerance_ratio": round(worst, 4),
+                   "within_tolerance": worst <= 1.0},
+    }
+    if not args.no_cpu_baseline:
+        # The oracle on a bounded sample: whole causal rows of the chunk, one at a time.
+        b = 0
+        c = int(w.context_lens[b])
+        r0, r1 = int(w.query_start[b]), int(w.query_start[b + 1])
+        kp = upcast(oracle.gather_sequence(w.k_cache, w.block_tables, b, c), w.dtype)
+        vpc = upcast(oracle.gather_sequence(w.v_cache, w.block_tables, b, c), w.dtype)
+        kn, vn = upcast(w.k_new, w.dtype), upcast(w.v_new, w.dtype)
+        qq = upcast(w.q, w.dtype)
+        try:
+            from threadpoolctl import threadpool_info, threadpool_limits
+            ctx = threadpool_limits(limits=len(os.sched_getaffinity(0)))
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:  # threadpoolctl missing: numpy picks its own thread count
+            ctx, threads = None, len(os.sched_getaffinity(0))
+        rows, fl, t1 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 10.0) and rows < r1 - r0:
+            i = rows
+            for h in range(w.num_q_heads):
+                g = h // G
+                ka = np.concatenate([kp[:, g], kn[r0:r0 + i + 1, g]])
+                va = np.concatenate([vpc[:, g], vn[r0:r0 + i + 1, g]])
+                oracle.prefill_rows(qq[r0 + i:r0 + i + 1, h], ka, va, c + i, s32)
+            fl += 4 * w.num_q_heads * w.head_dim * (c + i + 1)
+            rows += 1
+        el = time.perf_counter() - t1
+        if ctx is not None:
+            ctx.restore_original_limits()
+        rec["cpu_baseline"] = {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"{rows} query rows x {w.num_q_heads} heads of "
+                                         f"sequence 0 (float64 numpy oracle), {el:.1f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -319,6 +468,11 @@ def main():
         return
     if args.sweep_paths:
         sweep_paths()
+        return
+    if args.op == "prefill":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        bench_prefill(args)
         return
     if args.op == "copy_blocks":
         assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -301,6 +301,12 @@ pa_status_t pa_split_plan(const pa_dims_t* dims, int64_t max_context_len, int32_
  */
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, int64_t num_blocks,
                            const int32_t* block_pairs, int64_t num_pairs, void* stream);
+/* pa_copy_blocks plus start / stop timestamps (hipEvent_t, may be NULL) recorded by the
+ * runtime when the copy kernel starts and ends. */
+pa_status_t pa_copy_blocks_profiled(void* k_cache, void* v_cache, int64_t block_bytes,
+                                    int64_t num_blocks, const int32_t* block_pairs,
+                                    int64_t num_pairs, void* stream, void* start_event,
+                                    void* stop_event);
 
 /*
  * Paged prefix-prefill attention.  Source: project_6
@@ -340,8 +346,8 @@ pa_status_t pa_prefill(const pa_prefill_dims_t* dims, void* out, const void* q,
                        const void* v_cache, const int32_t* block_tables,
                        const int32_t* context_lens, const int32_t* query_start, float scale,
                        void* stream);
-/* pa_prefill plus runtime timestamps (hipEvent_t, may be NULL) recorded around the
- * kernel on the same stream. */
+/* pa_prefill plus start / stop timestamps (hipEvent_t, may be NULL) recorded by the
+ * runtime when the prefill kernel starts and ends. */
 pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const void* q,
                                 const void* k_new, const void* v_new, const void* k_cache,
                                 const void* v_cache, const int32_t* block_tables,

@@ -78,6 +78,7 @@ SIGNATURES = {
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
     "pa_split_plan": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P]),
+    "pa_copy_blocks_profiled": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "pa_prefill": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           ctypes.c_float, _P]),
     "pa_prefill_profiled": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P,

@@ -647,6 +647,14 @@ int32_t pa_get_mfma_variant(void) { return pa::get_mfma_variant(); }
 
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, int64_t num_blocks,
                            const int32_t* block_pairs, int64_t num_pairs, void* stream) {
+  return pa_copy_blocks_profiled(k_cache, v_cache, block_bytes, num_blocks, block_pairs,
+                                 num_pairs, stream, nullptr, nullptr);
+}
+
+pa_status_t pa_copy_blocks_profiled(void* k_cache, void* v_cache, int64_t block_bytes,
+                                    int64_t num_blocks, const int32_t* block_pairs,
+                                    int64_t num_pairs, void* stream, void* start_event,
+                                    void* stop_event) {
   try {
     if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %lld is negative", (long long)num_pairs);
     if (block_bytes <= 0 || block_bytes % 16 || block_bytes > (int64_t)0x7fffffff)
@@ -673,7 +681,9 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes, in
       return fail(PA_ERR_UNSUPPORTED, "%lld pairs of %d chunks exceed the grid limit",
                   (long long)num_pairs, a.chunks);
     return hip_status(pa::launch_copy_blocks(a, num_pairs, v_cache != nullptr,
-                                             static_cast<hipStream_t>(stream)),
+                                             static_cast<hipStream_t>(stream),
+                                             static_cast<hipEvent_t>(start_event),
+                                             static_cast<hipEvent_t>(stop_event)),
                       "block-copy launch");
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");

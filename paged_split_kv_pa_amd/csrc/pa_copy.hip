@@ -12,6 +12,7 @@
 // resources bounded to the block, so the last, shorter chunk needs no branches:
 // loads past the end return 0 and stores past the end are dropped.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,10 +56,10 @@ __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(const CopyArg
 int copy_chunk_bytes() { return kCopyThreads * kCopyVec * 16; }
 
 hipError_t launch_copy_blocks(const CopyArgs& a, long long num_pairs, bool with_v,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const long long wgs = num_pairs * a.chunks;
   const dim3 grid((unsigned)wgs, with_v ? 2 : 1, 1);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, a);
+  hipExtLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, e0, e1, 0, a);
   return hipGetLastError();
 }
 

@@ -90,8 +90,10 @@ struct CopyArgs {
 };
 int copy_chunk_bytes();
 // Grid (num_pairs * chunks, 1 or 2 pools).
+// ev_start / ev_stop (may be null) are recorded when the kernel starts / ends.
 hipError_t launch_copy_blocks(const CopyArgs& a, long long num_pairs, bool with_v,
-                              hipStream_t stream);
+                              hipStream_t stream, hipEvent_t ev_start = nullptr,
+                              hipEvent_t ev_stop = nullptr);
 
 // ---- paged prefix prefill (pa_prefill.hip) ---------------------------------------------
 struct PrefillArgs {
@@ -109,6 +111,7 @@ struct PrefillArgs {
 };
 int prefill_positions_per_workgroup(int group);
 // Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128, fp16/bf16.
+// e0 / e1 (may be null) are recorded when the kernel starts / ends.
 hipError_t launch_prefill(int dtype, int group, const PrefillArgs& a, int num_seqs,
                           int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1);
 

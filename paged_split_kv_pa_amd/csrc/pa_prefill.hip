@@ -28,6 +28,7 @@
 //                  so instruction j produces head-dim indices 8n + j.
 // The next tile's global loads are issued before the current tile's math.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -362,13 +363,15 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 }
 
 template <int DT>
-hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0,
+                    hipEvent_t e1) {
+  const dim3 block(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<DT, 8>), grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<DT, 16>), grid, dim3(256), 0, st, a); break;
+    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16>), grid, block, 0, st, e0, e1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -382,12 +385,9 @@ hipError_t launch_prefill(int dtype, int group, const PrefillArgs& a, int num_se
                           int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int per = kRows / group;
   const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
-  if (e0) (void)hipEventRecord(e0, stream);
-  hipError_t err = dtype == PA_BF16 ? launch_g<PA_BF16>(group, a, grid, stream)
-                 : dtype == PA_F16  ? launch_g<PA_F16>(group, a, grid, stream)
-                                    : hipErrorInvalidValue;
-  if (e1) (void)hipEventRecord(e1, stream);
-  return err;
+  return dtype == PA_BF16 ? launch_g<PA_BF16>(group, a, grid, stream, e0, e1)
+       : dtype == PA_F16  ? launch_g<PA_F16>(group, a, grid, stream, e0, e1)
+                          : hipErrorInvalidValue;
 }
 
 }  // namespace pa
