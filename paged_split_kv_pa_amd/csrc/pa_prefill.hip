@@ -217,122 +217,140 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       blk_next = fetch_block(t + 2);
     }
 
-    // Per tile: S^T for both 32-key halves (matrix cores), the row maxima over the 64
-    // keys and one rescale decision (VALU), then P and O += P V per half.  The PV
-    // products of the first half are interleaved with the exponentials of the second
-    // (scheduling groups), so the matrix cores and the VALU work at the same time.
+    // Per tile, the four column groups run as two independent pairs so that the matrix
+    // cores and the VALU overlap: the exponentials of pair 0 are interleaved with the
+    // QK^T products of pair 1, and the PV products of pair 0 with the exponentials of
+    // pair 1 (scheduling groups).  Each pair takes one row max over the whole 64-key tile
+    // and one rescale decision.
     const int kbase = t * kTile;
     const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
-    f32x4 S[2][2][4];  // [half][row block][column group]
+    u32x4 ka[4][4];  // [row block][k step]: the tile's K operands, shared by both pairs
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 ka[2][4];
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int kk = 0; kk < 4; ++kk) {
+        ka[rb][kk] = s_k[swz(16 * rb + r16, 4 * kk + kg)];
+        asm("" : "+a"(ka[rb][kk]));
+      }
+    auto qk = [&](int pr, f32x4 (&S)[4][2]) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          ka[h][kk] = s_k[swz(16 * (2 * s + h) + r16, 4 * kk + kg)];
-          asm("" : "+a"(ka[h][kk]));
-        }
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          S[s][h][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 2; ++q) {
+          S[rb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            S[s][h][cg] = mfma32<kBF>(ka[h][kk], qf[cg][kk], S[s][h][cg]);
+            S[rb][q] = mfma32<kBF>(ka[rb][kk], qf[2 * pr + q][kk], S[rb][q]);
         }
-    }
-
-    // Row maxima (base 2) over the tile; masked keys become -inf on diagonal tiles,
-    // where S then holds scaled logits (exp2 of -inf - m is 0).
-    float bm[4];
-    bool grow = false;
+    };
+    // Row max over the tile and the rescale for pair pr; masked keys become -inf on
+    // diagonal tiles, where S then holds scaled logits (exp2 of -inf - m is 0).
+    auto pair_max = [&](int pr, f32x4 (&S)[4][2]) {
+      float bm[2];
+      bool grow = false;
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      float mx = kNegInf;
+      for (int q = 0; q < 2; ++q) {
+        const int cg = 2 * pr + q;
+        float mx = kNegInf;
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int rb = 0; rb < 4; ++rb) {
           if (diag) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = kbase + 16 * (2 * s + h) + 4 * kg + i;
+              const int key = kbase + 16 * rb + 4 * kg + i;
               const bool vis = key <= c + qpos_col[cg] && key < nkeys;
-              S[s][h][cg][i] = vis ? S[s][h][cg][i] * sl : kNegInf;
+              S[rb][q][i] = vis ? S[rb][q][i] * sl : kNegInf;
             }
           }
-          mx = fmaxf(mx, fmaxf(fmaxf(S[s][h][cg][0], S[s][h][cg][1]),
-                               fmaxf(S[s][h][cg][2], S[s][h][cg][3])));
+          mx = fmaxf(mx, fmaxf(fmaxf(S[rb][q][0], S[rb][q][1]), fmaxf(S[rb][q][2], S[rb][q][3])));
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      bm[cg] = diag ? mx : mx * sl;
-      grow = grow || bm[cg] > m_ref[cg] + kRescaleSlack;
-    }
-    if (__any(grow)) {  // rare: one branch per tile for all column groups
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        const float m_new = fmaxf(m_ref[cg], bm[cg]);
-        const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
-        m_ref[cg] = m_new;
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        bm[q] = diag ? mx : mx * sl;
+        grow = grow || bm[q] > m_ref[cg] + kRescaleSlack;
       }
-    }
-
+      if (__any(grow)) {  // rare
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int cg = 2 * pr + q;
+          const float m_new = fmaxf(m_ref[cg], bm[q]);
+          const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
+          m_ref[cg] = m_new;
+          float al[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
+        }
+      }
+    };
     // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
-    auto probs = [&](int s, u32x4 (&Pa)[4]) {
+    // P of pair pr as PV A operands: Pa[q][s] covers keys of row blocks 2s, 2s+1.
+    auto probs = [&](int pr, const f32x4 (&S)[4][2], u32x4 (&Pa)[2][2]) {
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        const float nm = -m_ref[cg];
-        float p[2][4];
+      for (int q = 0; q < 2; ++q) {
+        const float nm = -m_ref[2 * pr + q];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int st = 0; st < 2; ++st) {
+          float p[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[s][h][cg][i], fs, nm));
-        Pa[cg] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
-                       pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[2 * st + h][q][i], fs, nm));
+          Pa[q][st] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
+                            pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+        }
       }
     };
-    auto pv = [&](int s, const u32x4 (&Pa)[4]) {
-      u32x4 run[8];
+    auto pv = [&](int pr, const u32x4 (&Pa)[2][2]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        run[e] = s_v[swz(16 * (2 * s + e / 4) + 4 * kg + (e & 3), r16)];
+      for (int st = 0; st < 2; ++st) {
+        u32x4 run[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
-                               __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+        for (int e = 0; e < 8; ++e)
+          run[e] = s_v[swz(16 * (2 * st + e / 4) + 4 * kg + (e & 3), r16)];
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) O[cg][j] = mfma32<kBF>(Pa[cg], bv, O[cg][j]);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
+                                 __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            O[2 * pr + q][j] = mfma32<kBF>(Pa[q][st], bv, O[2 * pr + q][j]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          Lacc[2 * pr + q] = mfma32<kBF>(Pa[q][st], ones, Lacc[2 * pr + q]);
       }
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) Lacc[cg] = mfma32<kBF>(Pa[cg], ones, Lacc[cg]);
     };
-    u32x4 P0[4], P1[4];
-    probs(0, P0);
+
+    f32x4 S0[4][2], S1[4][2];
+    u32x4 P0[2][2], P1[2][2];
+    qk(0, S0);
+    pair_max(0, S0);
+    probs(0, S0, P0);
+    qk(1, S1);
+    // pair 1's 32 QK^T products against pair 0's exponentials and packing
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    pair_max(1, S1);
     pv(0, P0);
-    probs(1, P1);
-    // Interleave: each of PV(0)'s 36 products followed by up to 3 VALU instructions of
-    // the second half's exponentials and packing.
+    probs(1, S1, P1);
+    // pair 0's 36 PV products against pair 1's exponentials and the V operand shuffles
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
     }
     pv(1, P1);
 #pragma unroll
