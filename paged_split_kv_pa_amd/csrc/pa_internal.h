@@ -75,7 +75,7 @@ Kernel kernel_for(int dtype, int group);
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
                             hipStream_t stream, hipEvent_t ev_start = nullptr,
                             hipEvent_t ev_stop = nullptr);
-// Launch the phase-2 kernel on grid (S*Hq, 8).
+// Launch the phase-2 kernel on grid (S*Hq, 8), or (S*Hq, 1) for many heads.
 hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
                          hipStream_t stream);
 

@@ -35,6 +35,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 
@@ -810,23 +811,23 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
 // r_q = exp(m_q - M) * s_q per partial state q, out = sum_q r_q o_q / sum_q r_q.
 // =======================================================================================
 constexpr int kMaxFold = kMaxReducePartitions + kMaxPieceSlots;  // partial states per head
-// Phase 2 splits each head's D columns over 8 work-groups: D/8 columns each (16 at
-// head_dim 128: 64 partition lanes x 4 float4 column lanes).  Phase 2 is bound by
-// per-CU load issue, so more, narrower work-groups finish sooner -- as long as the
-// grid stays small: at head_dim 256 with 16 columns its speculative loads cost more
-// than they save (measured).
-constexpr int kReduceChunks = 8;
+// Phase 2 splits each head's D columns over CHUNKS work-groups.  With few (sequence,
+// head) pairs, 8 chunks (16 columns at head_dim 128: 64 partition lanes x 4 float4
+// column lanes): phase 2 is bound by per-CU load issue, so more, narrower work-groups
+// finish sooner.  With many pairs (>= kReduceWideHeads), 1 chunk: the grid is already
+// large, and every extra work-group pays the fixed start-up latency.
+constexpr int kReduceWideHeads = 256;
 
-template <int DT, int D>
+template <int DT, int D, int CHUNKS>
 __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   // The weights r_q live in LDS (one per partial state); thread (pg, d4) then sums
   // r_q o_q over its partial states q = pg, pg+NPG, ... for 4 of the work-group's
   // kReduceCols columns, and the NPG partition lanes are summed in a fixed tree
   // (bitwise deterministic).
-  constexpr int kReduceCols = D / kReduceChunks;
+  constexpr int kReduceCols = D / CHUNKS;
   constexpr int NC4 = kReduceCols / 4;  // float4 column lanes
   constexpr int NPG = 256 / NC4;        // partition lanes
-  __shared__ float s_w[kMaxFold];
+  extern __shared__ float s_w[];        // one weight per partial state (sized at launch)
   __shared__ float s_red[4];
   __shared__ f32x4 s_acc[4][NC4];
   const int bh = blockIdx.x, chunk = blockIdx.y;
@@ -879,8 +880,9 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   // no arithmetic on them before the context length is known: a guarded or consumed
   // load would make the compiler wait for it before issuing the next one.
   // Output rows per thread (states pg + NPG i) loaded up front: 320 states cover the
-  // 196 partitions of a 100K-token context plus its cut items' pieces.
-  constexpr int kSpecO = 320 / NPG;
+  // 196 partitions of a 100K-token context plus its cut items' pieces (with one chunk,
+  // at most 8 rows per thread).
+  constexpr int kSpecO = CHUNKS == 1 ? (320 / NPG < 8 ? 320 / NPG : 8) : 320 / NPG;
   constexpr int kSpecMS = 2;  // statistics per thread: partial states tid + 256 j
   f32x4 so[kSpecO];
   float sm[kSpecMS], ss[kSpecMS];
@@ -1054,19 +1056,31 @@ hipError_t launch_attn_d(int D, int G, const AttnArgs& a, const Launch& l) {
   return hipErrorInvalidValue;
 }
 
-template <int DT>
-hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
-  dim3 block(256);
-  if (D == 128) {
-    dim3 grid((unsigned)(S * a.Hq), kReduceChunks);
-    hipLaunchKernelGGL((reduce_kernel<DT, 128>), grid, block, 0, st, a);
-  } else if (D == 256) {
-    dim3 grid((unsigned)(S * a.Hq), kReduceChunks);
-    hipLaunchKernelGGL((reduce_kernel<DT, 256>), grid, block, 0, st, a);
+template <int DT, int D>
+hipError_t launch_reduce_dd(const ReduceArgs& a, int S, hipStream_t st) {
+  // LDS: one float per partial state of a head: partitions, plus the pieces of cut ones.
+  long long fold = a.Pmax;
+  if (a.split.shift > 0) {
+    const long long items = (long long)a.Pmax * a.Hkv * S;
+    const long long cut = (items - a.split.first) << a.split.shift;
+    fold += std::min(cut, (long long)a.Pmax << a.split.shift);
+  }
+  if (fold > kMaxFold) return hipErrorInvalidValue;
+  const size_t lds = (size_t)fold * sizeof(float);
+  const long long heads = (long long)S * a.Hq;
+  if (heads >= kReduceWideHeads) {
+    hipLaunchKernelGGL((reduce_kernel<DT, D, 1>), dim3((unsigned)heads, 1), dim3(256), lds, st, a);
   } else {
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((reduce_kernel<DT, D, 8>), dim3((unsigned)heads, 8), dim3(256), lds, st, a);
   }
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
+  if (D == 128) return launch_reduce_dd<DT, 128>(a, S, st);
+  if (D == 256) return launch_reduce_dd<DT, 256>(a, S, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
