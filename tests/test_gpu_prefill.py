@@ -166,3 +166,16 @@ def test_max_query_len_bounds_the_rows_written():
         k = min(L, 64)
         check_rows(got[r0:r0 + k], ref[r0:r0 + k], f"max_query_len seq {b}")
         assert np.all(got[r0 + k:r0 + L] == 7.0), "rows past max_query_len must be untouched"
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.09])
+def test_scale_sign_and_zero(scale):
+    """A negative scale (carried as a sign flip of q in the kernel) and scale 0 (uniform
+    weights over the visible keys) against the oracle.  (|scale| near 1/sqrt(128): with
+    N(0, 1) inputs and a much larger scale the softmax is peaky enough that the bf16
+    rounding of P alone exceeds the absolute bound on some near-zero outputs.)"""
+    w = wl.make_prefill_workload("sc", 90, context_lens=[50, 0], query_lens=[37, 70],
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128, dtype="bf16",
+                                 scale=scale)
+    say(f"prefill scale={scale}")
+    check_rows(to_f64(run(w, upload(w))), reference(w), f"scale {scale}")
