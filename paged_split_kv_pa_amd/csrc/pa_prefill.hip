@@ -64,17 +64,46 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest-even 16-bit values, lo in the low half (one
+// v_cvt_pk_{bf16,f16}_f32).
 template <bool BF>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  uint16_t l, h;
-  if constexpr (BF) {
-    l = __builtin_bit_cast(uint16_t, (__bf16)lo);
-    h = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  } else {
-    l = __builtin_bit_cast(uint16_t, (_Float16)lo);
-    h = __builtin_bit_cast(uint16_t, (_Float16)hi);
-  }
-  return (uint32_t)l | ((uint32_t)h << 16);
+  const f32x2 v = {lo, hi};
+  if constexpr (BF)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of one MFMA column),
+// with the two gfx950 half-swaps (upper 32 lanes with lower 32, odd 16-lane rows with
+// even ones).  The swapped pair is passed through an empty asm: without it the compiler
+// (ROCm 7.2) emitted the float max of the two results with the same register twice.
+__device__ __forceinline__ float max_over_groups(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  uint32_t a0 = a[0], a1 = a[1];
+  asm("" : "+v"(a0), "+v"(a1));
+  u = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1)));
+  const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  uint32_t b0 = b[0], b1 = b[1];
+  asm("" : "+v"(b0), "+v"(b1));
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane j
+// receives element j % 4 of the 8-byte rows read by lanes 4e + j / 4, e = 0..3 (the
+// lane layout was checked on the device with an in-bounds probe).
+__device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // LDS slot (in 16-byte units) of chunk `c` of tile row `r`.
@@ -264,8 +293,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
           }
           mx = fmaxf(mx, fmaxf(fmaxf(S[rb][q][0], S[rb][q][1]), fmaxf(S[rb][q][2], S[rb][q][3])));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_groups(mx);
         bm[q] = diag ? mx : mx * sl;
         grow = grow || bm[q] > m_ref[cg] + kRescaleSlack;
       }
@@ -307,24 +335,33 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
         }
       }
     };
+    // V operands of the tile: vb[st][jd] = B of the 32 keys of step st (in the P k-slot
+    // order) x head-dim 16 jd + (0..15).  Lane (j, kg) reads 8 bytes of key
+    // 32 st + 4 kg + j / 4 (+16 for the second read), head-dim 16 jd + 4 (j % 4), and the
+    // transposing read hands lane (n, kg) the 4 keys of its k-slots at head-dim 16 jd + n.
+    u32x4 vb[2][8];
+    auto load_v = [&]() {
+      const char* vbase = reinterpret_cast<const char*>(s_v);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+          const int key = 32 * st + 4 * kg + (r16 >> 2);
+          const int c = 2 * jd + ((r16 & 3) >> 1), half = r16 & 1;
+          const u32x2 lo = lds_read_tr(vbase + swz(key, c) * 16 + half * 8);
+          const u32x2 hi = lds_read_tr(vbase + swz(key + 16, c) * 16 + half * 8);
+          vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          asm("" : "+a"(vb[st][jd]));
+        }
+    };
     auto pv = [&](int pr, const u32x4 (&Pa)[2][2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        u32x4 run[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          run[e] = s_v[swz(16 * (2 * st + e / 4) + 4 * kg + (e & 3), r16)];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-          const u32x4 bv = u32x4{__builtin_amdgcn_perm(run[1][j >> 1], run[0][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[3][j >> 1], run[2][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[5][j >> 1], run[4][j >> 1], sel),
-                                 __builtin_amdgcn_perm(run[7][j >> 1], run[6][j >> 1], sel)};
+        for (int jd = 0; jd < 8; ++jd)
 #pragma unroll
           for (int q = 0; q < 2; ++q)
-            O[2 * pr + q][j] = mfma32<kBF>(Pa[q][st], bv, O[2 * pr + q][j]);
-        }
+            O[2 * pr + q][jd] = mfma32<kBF>(Pa[q][st], vb[st][jd], O[2 * pr + q][jd]);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           Lacc[2 * pr + q] = mfma32<kBF>(Pa[q][st], ones, Lacc[2 * pr + q]);
@@ -343,6 +380,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
+    load_v();
     pair_max(1, S1);
     pv(0, P0);
     probs(1, S1, P1);
@@ -359,7 +397,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       for (int j = 0; j < 8; ++j) asm("" : "+v"(O[cg][j]));
   }
 
-  // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 8 r16 .. +7 ----
+  // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) {
 #pragma unroll
@@ -371,11 +409,12 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
       const int hq = g * G + row % G;
       const float inv = 1.f / li;
       uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * kD;
-      *reinterpret_cast<u32x4*>(orow + 8 * r16) =
-          u32x4{pack2<kBF>(O[cg][0][i] * inv, O[cg][1][i] * inv),
-                pack2<kBF>(O[cg][2][i] * inv, O[cg][3][i] * inv),
-                pack2<kBF>(O[cg][4][i] * inv, O[cg][5][i] * inv),
-                pack2<kBF>(O[cg][6][i] * inv, O[cg][7][i] * inv)};
+#pragma unroll
+      for (int jd = 0; jd < 8; jd += 2) {
+        const uint32_t two = pack2<kBF>(O[cg][jd][i] * inv, O[cg][jd + 1][i] * inv);
+        orow[16 * jd + r16] = (uint16_t)two;
+        orow[16 * (jd + 1) + r16] = (uint16_t)(two >> 16);
+      }
     }
   }
 }
