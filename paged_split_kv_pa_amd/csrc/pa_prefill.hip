@@ -225,8 +225,6 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
     for (int i = 0; i < 4; ++i) {
       kr[i] = *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i));
       vr[i] = *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i));
-      asm("" : "+a"(kr[i]));
-      asm("" : "+a"(vr[i]));
     }
   };
 
@@ -234,11 +232,19 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
   load_tile(0, fetch_block(0));
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();  // the previous tile's LDS reads are done
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (__all(row_ok)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_k[swz(lrow, lc0 + i)] = row_ok ? kr[i] : z;
-      s_v[swz(lrow, lc0 + i)] = row_ok ? vr[i] : z;
+      for (int i = 0; i < 4; ++i) {
+        s_k[swz(lrow, lc0 + i)] = kr[i];
+        s_v[swz(lrow, lc0 + i)] = vr[i];
+      }
+    } else {  // tail tile, or a prefix row with an out-of-range block id
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_k[swz(lrow, lc0 + i)] = row_ok ? kr[i] : z;
+        s_v[swz(lrow, lc0 + i)] = row_ok ? vr[i] : z;
+      }
     }
     __syncthreads();
     if (t + 1 < ntiles) {  // in flight during this tile's math
