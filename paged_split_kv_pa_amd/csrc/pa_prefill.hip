@@ -7,26 +7,32 @@
 // oracle): new token i of sequence b (absolute position c_b + i) attends to the c_b
 // prefix tokens in the paged cache and to new tokens 0..i, whose K/V arrive packed.
 //
-// Work-group: 4 waves, 256 query rows of one KV head g of one sequence: positions
+// Work-group: 8 waves, 256 query rows of one KV head g of one sequence: positions
 // [p0, p0 + 256/G) x the G query heads of g, row r = (position p0 + r / G, head
 // g*G + r % G).  Sharing every K/V tile among the G heads and 256/G positions is what
-// makes the tile traffic small next to the MFMA work.  Wave w owns rows 64w..64w+63,
-// as four column groups of 16 rows (the MFMA's 16 columns).
+// makes the tile traffic small next to the MFMA work.  Wave w owns rows 32w..32w+31,
+// as two column groups of 16 rows (the MFMA's 16 columns).
+//
+// Two waves share each SIMD, and they take turns: the work of a wave alternates between
+// a matrix phase (O += P V for the previous tile, then S^T = K Q^T for this one) and a
+// softmax phase (row max, rescale, P = exp2(...)), and waves 0-3 run their matrix phase
+// while waves 4-7 run their softmax phase and the other way round, with a work-group
+// barrier between phases.  So the matrix cores of a SIMD are fed by one wave while the
+// other one's exponentials run on the VALU.
 //
 // Per 64-key tile: K and V rows are loaded from the cache (key < c, through the
-// block table) or from the packed new tokens (c <= key < c + L), into LDS rows of
-// 256 bytes whose 16-byte chunks are XOR-swizzled with the row index, so that both
-// operand reads below hit 16 distinct chunk positions per 16 lanes.
-//   S^T = K Q^T:   v_mfma_f32_16x16x32, A = 16 keys x 32 dims (LDS), B = Q (registers):
+// block table) or from the packed new tokens (c <= key < c + L), into padded LDS rows.
+//   S^T = K Q^T:   v_mfma_f32_16x16x32, A = 16 keys x 32 dims, B = Q (both from LDS,
+//                  where the work-group's 256 query rows are staged once):
 //                  lane (r16, kg) gets keys 4kg..4kg+3 of query row r16.
 //   online softmax per query row in base 2 (scale * log2 e folded in), causal mask on
 //                  the tiles that reach the row's own position, lazy rescale as in decode.
 //   O += P V:      v_mfma_f32_16x16x32 over 32 keys = two 16-key row blocks: the S^T
 //                  accumulators of the two blocks are exactly the A operand (k-slot e of
-//                  lane group kg is key 16(2s + e/4) + 4kg + e%4), and the B operand
-//                  takes column j of the 16-byte V runs of those 8 keys (v_perm pairs),
-//                  so instruction j produces head-dim indices 8n + j.
-// The next tile's global loads are issued before the current tile's math.
+//                  lane group kg is key 16(2s + e/4) + 4kg + e%4); the B operand comes
+//                  from V in LDS through the gfx950 transposing read, in that key order.
+// K and V have two LDS buffers each; a tile's K is written one phase before its first
+// QK^T and its V one phase before its first PV, from loads issued two phases earlier.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -49,6 +55,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;
 constexpr int kD = 128;          // head_dim built
 constexpr int kRows = 256;       // query rows per work-group
+constexpr int kThreads = 512;    // 8 waves of 32 rows
 constexpr int kTile = 64;        // keys per K/V tile
 constexpr int kChunks = kD / 8;  // 16-byte chunks per row
 
@@ -106,15 +113,20 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// LDS slot (in 16-byte units) of chunk `c` of tile row `r`.
-__device__ __forceinline__ int swz(int r, int c) { return r * kChunks + (c ^ (r & 15)); }
+// LDS rows are padded so that both operand reads are free of bank conflicts with plain
+// linear addresses: K rows take 272 bytes (16 rows of one 16-lane K read land 16 bytes
+// apart), V rows 288 bytes (the 8 rows of a half-wave's transposing read land 32 bytes
+// apart).
+constexpr int kKRow = kChunks + 1;  // K row stride in 16-byte units
+constexpr int kVRow = kChunks + 2;  // V row stride in 16-byte units
 
 template <int DT, int G>
-__global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
   constexpr int kPos = kRows / G;  // query positions per work-group
-  __shared__ u32x4 s_k[kTile * kChunks];
-  __shared__ u32x4 s_v[kTile * kChunks];
+  __shared__ u32x4 s_q[kRows * kKRow];
+  __shared__ u32x4 s_k[2][kTile * kKRow];
+  __shared__ u32x4 s_v[2][kTile * kVRow];
 
   const int g = blockIdx.y, b = blockIdx.z;
   const int p0 = blockIdx.x * kPos;
@@ -129,6 +141,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;  // 0: matrix phases on even phase numbers, 1: on odd ones
   const int lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
 
@@ -137,68 +150,53 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
   const int nkeys = c + pend;
   const int ntiles = (nkeys + kTile - 1) / kTile;
 
-  // ---- query operands and per-row state ----
-  // Column group cg of this wave: rows 64w + 16cg + (0..15); lane column r16.
-  u32x4 qf[4][4];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
-  int qpos_col[4];
-#pragma unroll
-  for (int cg = 0; cg < 4; ++cg) {
-    const int row = 64 * w + 16 * cg + r16;
+  // ---- queries in LDS (rows of 272 bytes, like K), per-row state ----
+  // Thread tid copies 64 bytes (4 chunks) of work-group row tid / 2; a negative scale is
+  // carried by flipping the sign of q (exact in 16-bit floats), since the softmax works
+  // on raw dot products scaled by |scale| log2(e): max(scale * s) is |scale| * max of the
+  // flipped products.  Rows past the last position are zero.
+  {
+    const int row = tid >> 1, c0 = (tid & 1) * 8;
     const int pos = p0 + row / G;
     const int hq = g * G + row % G;
-    qpos_col[cg] = pos;
     const bool valid = pos < L;
     const uint16_t* qrow =
         static_cast<const uint16_t*>(a.q) + ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * kD;
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qf[cg][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
-                         : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      u32x4 v = valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * (c0 + i)) : u32x4{0u, 0u, 0u, 0u};
+      s_q[row * kKRow + c0 + i] = v ^ u32x4{flip, flip, flip, flip};
+    }
   }
-  // The softmax works on raw dot products scaled by |scale| log2(e); a negative scale is
-  // carried by flipping the sign of q (exact in 16-bit floats), so max(scale * s) is
-  // |scale| * max of the flipped products.
   const float sl = fabsf(a.scale_log2);
-  if (a.scale_log2 < 0.f) {
-    const uint32_t flip = 0x80008000u;
+  int qpos_col[2];  // position of query row r16 of column group cg
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
+  for (int cg = 0; cg < 2; ++cg) qpos_col[cg] = p0 + (32 * w + 16 * cg + r16) / G;
+  // Q operand of column group cg, k step kk: Q[row 32w + 16cg + r16][32kk + 8kg .. +7].
+  const u32x4* qbase = s_q + (32 * w + r16) * kKRow + kg;
+  f32x4 O[2][8];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[cg][kk] ^= u32x4{flip, flip, flip, flip};
-  }
-  // Register classes, pinned with empty asm constraints: the output and score
-  // accumulators live in VGPRs (the softmax and the rare rescale work on them there),
-  // while MFMA input operands (queries, K rows) and the staged tile loads live in AGPRs.
-  // Left to itself the compiler kept the output accumulators in AGPRs and copied all
-  // 128 of them to VGPRs and back on every tile.
-#pragma unroll
-  for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) asm("" : "+a"(qf[cg][kk]));
-  f32x4 O[4][8];
-#pragma unroll
-  for (int cg = 0; cg < 4; ++cg)
+  for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
     for (int j = 0; j < 8; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Row sums of P come from the matrix cores too: one more PV product per column group
   // with an all-ones B operand leaves sum_k P[row][k] in every column, in the same
   // row layout as O (and from the same bf16-rounded P as O).
-  f32x4 Lacc[4];
-  float m_ref[4];
+  f32x4 Lacc[2];
+  float m_ref[2];
 #pragma unroll
-  for (int cg = 0; cg < 4; ++cg) {
+  for (int cg = 0; cg < 2; ++cg) {
     m_ref[cg] = kNegInf;
     Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint32_t one2 = kBF ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0
   const u32x4 ones = {one2, one2, one2, one2};
 
-  // ---- tile loads: thread tid moves 64 bytes (4 chunks) of K and of V of tile row tid/4 ----
+  // ---- tile loads: thread tid moves 32 bytes (2 chunks) of K and of V of tile row tid/8 ----
   // Loads are unconditional (a row outside the keys reads a valid dummy row and is
-  // zeroed when written to LDS), so no branch or wait sits between them.  The block id
-  // of a prefix row is read two tiles ahead, behind the K/V loads of the next tile:
-  // consuming it never drains loads that are still useful in flight.
-  const int lrow = tid >> 2, lc0 = (tid & 3) * 4;
+  // zeroed when written to LDS).  Block ids are read one tile ahead of their use.
+  const int lrow = tid >> 3, lc0 = (tid & 7) * 2;
   const size_t hstride = (size_t)kBlockSize * kD;  // elements per (block, head)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
@@ -210,206 +208,240 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
   auto fetch_block = [&](int t) {  // block id of this thread's row of tile t (any if not prefix)
     return btrow[min(t * kTile + lrow, cmax) / kBlockSize];
   };
-  u32x4 kr[4], vr[4];
-  bool row_ok = false;
-  auto load_tile = [&](int t, int blk) {
+  // Row lrow of tile t: source element offset in the cache (pre) or the new tokens.
+  auto row_source = [&](int t, int blk, bool& pre, bool& ok) -> size_t {
     const int key = t * kTile + lrow;
-    const bool pre = key < c && (unsigned)blk < (unsigned)a.NB;
+    pre = key < c && (unsigned)blk < (unsigned)a.NB;
     const bool fresh = key >= c && key < nkeys;
-    row_ok = pre || fresh;
-    const size_t off = pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD
-                           : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * kD : (size_t)r0 * a.Hkv * kD);
-    const uint16_t* ks = (pre ? kc : knew) + off;
-    const uint16_t* vs = (pre ? vc : vnew) + off;
+    ok = pre || fresh;
+    return pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD
+               : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * kD : (size_t)r0 * a.Hkv * kD);
+  };
+  u32x4 kr[2], vr[2];
+  bool ok_k = false, ok_v = false;
+  auto load_k = [&](int t, int blk) {
+    bool pre;
+    const size_t off = row_source(t, blk, pre, ok_k);
+    const uint16_t* src = (pre ? kc : knew) + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = *reinterpret_cast<const u32x4*>(ks + 8 * (lc0 + i));
-      vr[i] = *reinterpret_cast<const u32x4*>(vs + 8 * (lc0 + i));
-    }
+    for (int i = 0; i < 2; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc0 + i));
+  };
+  auto load_v = [&](int t, int blk) {
+    bool pre;
+    const size_t off = row_source(t, blk, pre, ok_v);
+    const uint16_t* src = (pre ? vc : vnew) + off;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc0 + i));
+  };
+  auto store_rows = [&](u32x4* dst, int stride, const u32x4 (&r)[2], bool ok) {
+    const u32x4 z = {0u, 0u, 0u, 0u};  // zero: tail rows, prefix rows with a bad block id
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dst[lrow * stride + lc0 + i] = ok ? r[i] : z;
   };
 
-  int blk_next = fetch_block(1);
-  load_tile(0, fetch_block(0));
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    if (__all(row_ok)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_k[swz(lrow, lc0 + i)] = kr[i];
-        s_v[swz(lrow, lc0 + i)] = vr[i];
-      }
-    } else {  // tail tile, or a prefix row with an out-of-range block id
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_k[swz(lrow, lc0 + i)] = row_ok ? kr[i] : z;
-        s_v[swz(lrow, lc0 + i)] = row_ok ? vr[i] : z;
-      }
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) {  // in flight during this tile's math
-      load_tile(t + 1, blk_next);
-      blk_next = fetch_block(t + 2);
-    }
+  {
+    const int blk0 = fetch_block(0);
+    load_k(0, blk0);
+    load_v(0, blk0);
+    store_rows(s_k[0], kKRow, kr, ok_k);
+    store_rows(s_v[0], kVRow, vr, ok_v);
+  }
+  int blk_k = fetch_block(1), blk_v = blk_k;
+  load_k(1, blk_k);
+  load_v(1, blk_v);
+  blk_k = fetch_block(2);
+  blk_v = blk_k;
+  __syncthreads();
 
-    // Per tile, the four column groups run as two independent pairs so that the matrix
-    // cores and the VALU overlap: the exponentials of pair 0 are interleaved with the
-    // QK^T products of pair 1, and the PV products of pair 0 with the exponentials of
-    // pair 1 (scheduling groups).  Each pair takes one row max over the whole 64-key tile
-    // and one rescale decision.
-    const int kbase = t * kTile;
-    const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
-    u32x4 ka[4][4];  // [row block][k step]: the tile's K operands, shared by both pairs
+  f32x4 S[4][2];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
+  u32x4 P[2][2];  // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1)
+
+  // S^T of tile t.
+  auto qk = [&](int t) {
+    const u32x4* kb = s_k[t & 1];
+    u32x4 qv[2][4], ka[4][4];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qv[cg][kk] = qbase[16 * cg * kKRow + 4 * kk];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        ka[rb][kk] = s_k[swz(16 * rb + r16, 4 * kk + kg)];
-        asm("" : "+a"(ka[rb][kk]));
+      for (int kk = 0; kk < 4; ++kk) ka[rb][kk] = kb[(16 * rb + r16) * kKRow + 4 * kk + kg];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) S[rb][cg] = mfma32<kBF>(ka[rb][kk], qv[cg][kk], S[rb][cg]);
       }
-    auto qk = [&](int pr, f32x4 (&S)[4][2]) {
+    // the reads of the next row block's K run under the current row block's products
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 3; ++rb) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  // O += P V for tile t.  V operand [st][jd]: the 32 keys of step st (in the P k-slot
+  // order) x head-dim 16 jd + (0..15); lane (j, kg) reads 8 bytes of key
+  // 32 st + 4 kg + j / 4 (+16 for the second read), head-dim 16 jd + 4 (j % 4), and the
+  // transposing read hands lane (n, kg) the 4 keys of its k-slots at head-dim 16 jd + n.
+  auto pv = [&](int t) {
+    const char* vbase = reinterpret_cast<const char*>(s_v[t & 1]);
+    u32x4 vb[2][8];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          S[rb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            S[rb][q] = mfma32<kBF>(ka[rb][kk], qf[2 * pr + q][kk], S[rb][q]);
-        }
-    };
-    // Row max over the tile and the rescale for pair pr; masked keys become -inf on
-    // diagonal tiles, where S then holds scaled logits (exp2 of -inf - m is 0).
-    auto pair_max = [&](int pr, f32x4 (&S)[4][2]) {
-      float bm[2];
-      bool grow = false;
+      for (int jd = 0; jd < 8; ++jd) {
+        const int key = 32 * st + 4 * kg + (r16 >> 2);
+        const char* src = vbase + key * (kVRow * 16) + 32 * jd + 8 * (r16 & 3);
+        const u32x2 lo = lds_read_tr(src);
+        const u32x2 hi = lds_read_tr(src + 16 * kVRow * 16);
+        vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int cg = 2 * pr + q;
-        float mx = kNegInf;
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          if (diag) {
+      for (int jd = 0; jd < 8; ++jd)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kbase + 16 * rb + 4 * kg + i;
-              const bool vis = key <= c + qpos_col[cg] && key < nkeys;
-              S[rb][q][i] = vis ? S[rb][q][i] * sl : kNegInf;
-            }
+        for (int cg = 0; cg < 2; ++cg) O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) Lacc[cg] = mfma32<kBF>(P[cg][st], ones, Lacc[cg]);
+    }
+    // V reads run two operands ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 14; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  // Softmax of tile t: row max (masked keys become -inf on diagonal tiles, where S then
+  // holds scaled logits), the rescale of O when a row max grows past the slack, and P.
+  auto softmax = [&](int t) {
+    const int kbase = t * kTile;
+    const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
+    float bm[2];
+    bool grow = false;
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (diag) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 16 * rb + 4 * kg + i;
+            const bool vis = key <= c + qpos_col[cg] && key < nkeys;
+            S[rb][cg][i] = vis ? S[rb][cg][i] * sl : kNegInf;
           }
-          mx = fmaxf(mx, fmaxf(fmaxf(S[rb][q][0], S[rb][q][1]), fmaxf(S[rb][q][2], S[rb][q][3])));
         }
-        mx = max_over_groups(mx);
-        bm[q] = diag ? mx : mx * sl;
-        grow = grow || bm[q] > m_ref[cg] + kRescaleSlack;
+        mx = fmaxf(mx, fmaxf(fmaxf(S[rb][cg][0], S[rb][cg][1]), fmaxf(S[rb][cg][2], S[rb][cg][3])));
       }
-      if (__any(grow)) {  // rare
+      mx = max_over_groups(mx);
+      bm[cg] = diag ? mx : mx * sl;
+      grow = grow || bm[cg] > m_ref[cg] + kRescaleSlack;
+    }
+    if (__any(grow)) {  // rare
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int cg = 2 * pr + q;
-          const float m_new = fmaxf(m_ref[cg], bm[q]);
-          const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
-          m_ref[cg] = m_new;
-          float al[4];
+      for (int cg = 0; cg < 2; ++cg) {
+        const float m_new = fmaxf(m_ref[cg], bm[cg]);
+        const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
+        m_ref[cg] = m_new;
+        float al[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
+          for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
-        }
+        for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
       }
-    };
+    }
     // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
-    // P of pair pr as PV A operands: Pa[q][s] covers keys of row blocks 2s, 2s+1.
-    auto probs = [&](int pr, const f32x4 (&S)[4][2], u32x4 (&Pa)[2][2]) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float nm = -m_ref[2 * pr + q];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          float p[2][4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[2 * st + h][q][i], fs, nm));
-          Pa[q][st] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
-                            pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
-        }
-      }
-    };
-    // V operands of the tile: vb[st][jd] = B of the 32 keys of step st (in the P k-slot
-    // order) x head-dim 16 jd + (0..15).  Lane (j, kg) reads 8 bytes of key
-    // 32 st + 4 kg + j / 4 (+16 for the second read), head-dim 16 jd + 4 (j % 4), and the
-    // transposing read hands lane (n, kg) the 4 keys of its k-slots at head-dim 16 jd + n.
-    u32x4 vb[2][8];
-    auto load_v = [&]() {
-      const char* vbase = reinterpret_cast<const char*>(s_v);
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int jd = 0; jd < 8; ++jd) {
-          const int key = 32 * st + 4 * kg + (r16 >> 2);
-          const int c = 2 * jd + ((r16 & 3) >> 1), half = r16 & 1;
-          const u32x2 lo = lds_read_tr(vbase + swz(key, c) * 16 + half * 8);
-          const u32x2 hi = lds_read_tr(vbase + swz(key + 16, c) * 16 + half * 8);
-          vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          asm("" : "+a"(vb[st][jd]));
-        }
-    };
-    auto pv = [&](int pr, const u32x4 (&Pa)[2][2]) {
+    for (int cg = 0; cg < 2; ++cg) {
+      const float nm = -m_ref[cg];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
+        float p[2][4];
 #pragma unroll
-        for (int jd = 0; jd < 8; ++jd)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-            O[2 * pr + q][jd] = mfma32<kBF>(Pa[q][st], vb[st][jd], O[2 * pr + q][jd]);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          Lacc[2 * pr + q] = mfma32<kBF>(Pa[q][st], ones, Lacc[2 * pr + q]);
+          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[2 * st + h][cg][i], fs, nm));
+        P[cg][st] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
+                          pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
       }
-    };
+    }
+  };
 
-    f32x4 S0[4][2], S1[4][2];
-    u32x4 P0[2][2], P1[2][2];
-    qk(0, S0);
-    pair_max(0, S0);
-    probs(0, S0, P0);
-    qk(1, S1);
-    // pair 1's 32 QK^T products against pair 0's exponentials and packing
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-    load_v();
-    pair_max(1, S1);
-    pv(0, P0);
-    probs(1, S1, P1);
-    // pair 0's 36 PV products against pair 1's exponentials and the V operand shuffles
-#pragma unroll
-    for (int k = 0; k < 36; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
-    }
-    pv(1, P1);
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) asm("" : "+v"(O[cg][j]));
+  // Phases: wave group grp runs the matrix work of tile t in phase 2t + grp and the
+  // softmax of tile t in phase 2t + grp + 1; a barrier ends every phase.  Tile traffic,
+  // the same in every wave: phase 2u + 1 writes K of tile u + 1 and requests K of tile
+  // u + 2; phase 2u + 2 writes V of tile u + 1 and requests V of tile u + 2.  K of tile u
+  // is read in phases 2u and 2u + 1, V of tile u in phases 2u + 2 and 2u + 3, so two
+  // buffers of each hold.
+  // Tile traffic of a phase: write tile u + 1 to LDS, request tile u + 2.  Both happen
+  // in every phase, also past the last tile (the buffer written is not read again, the
+  // rows requested are valid dummy rows): with no branch around them the compiler's wait
+  // counts stay exact, and no wait drains the loads still in flight.
+  auto io_k = [&](int u) {
+    store_rows(s_k[(u + 1) & 1], kKRow, kr, ok_k);
+    load_k(u + 2, blk_k);
+    blk_k = fetch_block(u + 3);
+  };
+  auto io_v = [&](int u) {
+    store_rows(s_v[(u + 1) & 1], kVRow, vr, ok_v);
+    load_v(u + 2, blk_v);
+    blk_v = fetch_block(u + 3);
+  };
+  // One tile t of wave group GRP: the matrix phase 2t + GRP, then the softmax phase
+  // 2t + GRP + 1.  Group 0 carries the V traffic in its matrix phase and the K traffic
+  // in its softmax phase, group 1 the other way round, so that every phase has the
+  // same traffic in all waves; the loop is written once per group.
+#define PA_TILE(GRP, T)                                                               \
+  do {                                                                                 \
+    const int t_ = (T);                                                                \
+    if (t_ >= 1) pv(t_ - 1);                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    if (t_ < ntiles) qk(t_);                                                           \
+    _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                  \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j) asm("" : "+v"(O[cg][j]));          \
+    if (GRP == 0) {                                                                    \
+      if (t_ >= 1) io_v(t_ - 1); /* phase 0 has no traffic */                          \
+    } else {                                                                           \
+      io_k(t_);                                                                        \
+    }                                                                                  \
+    __syncthreads();                                                                   \
+    if (t_ < ntiles) softmax(t_);                                                      \
+    if (GRP == 0)                                                                      \
+      io_k(t_);                                                                        \
+    else                                                                               \
+      io_v(t_);                                                                        \
+    __syncthreads();                                                                   \
+  } while (0)
+  if (grp == 0) {
+    for (int t = 0; t <= ntiles; ++t) PA_TILE(0, t);
+    __syncthreads();  // the last phase: group 1's final PV
+  } else {
+    __syncthreads();  // phase 0: group 0's first QK^T
+    for (int t = 0; t <= ntiles; ++t) PA_TILE(1, t);
   }
+#undef PA_TILE
 
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
-  for (int cg = 0; cg < 4; ++cg) {
+  for (int cg = 0; cg < 2; ++cg) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float li = Lacc[cg][i];
-      const int row = 64 * w + 16 * cg + 4 * kg + i;
+      const int row = 32 * w + 16 * cg + 4 * kg + i;
       const int pos = p0 + row / G;
       if (pos >= L) continue;
       const int hq = g * G + row % G;
@@ -428,7 +460,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(const PrefillArgs a) {
 template <int DT>
 hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0,
                     hipEvent_t e1) {
-  const dim3 block(256);
+  const dim3 block(kThreads);
   switch (G) {
     case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1>), grid, block, 0, st, e0, e1, 0, a); break;
     case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2>), grid, block, 0, st, e0, e1, 0, a); break;
