@@ -113,11 +113,12 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// LDS rows are padded so that both operand reads are free of bank conflicts with plain
-// linear addresses: K rows take 272 bytes (16 rows of one 16-lane K read land 16 bytes
-// apart), V rows 288 bytes (the 8 rows of a half-wave's transposing read land 32 bytes
-// apart).
-constexpr int kKRow = kChunks + 1;  // K row stride in 16-byte units
+// LDS rows of K, V and Q are padded to 288 bytes, which leaves all three operand reads
+// free of bank conflicts with plain linear addresses (measured with the LDS bank-conflict
+// counter: the 16-byte reads of 16 rows per K / Q operand, and the 8-byte transposing
+// reads of 8 rows per half-wave for V; a 256-byte row conflicts 28 cycles per read, a
+// 272-byte row 4).
+constexpr int kKRow = kChunks + 2;  // K and Q row stride in 16-byte units
 constexpr int kVRow = kChunks + 2;  // V row stride in 16-byte units
 
 template <int DT, int G>
@@ -150,7 +151,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   const int nkeys = c + pend;
   const int ntiles = (nkeys + kTile - 1) / kTile;
 
-  // ---- queries in LDS (rows of 272 bytes, like K), per-row state ----
+  // ---- queries in LDS (rows of 288 bytes, like K), per-row state ----
   // Thread tid copies 64 bytes (4 chunks) of work-group row tid / 2; a negative scale is
   // carried by flipping the sign of q (exact in 16-bit floats), since the softmax works
   // on raw dot products scaled by |scale| log2(e): max(scale * s) is |scale| * max of the
