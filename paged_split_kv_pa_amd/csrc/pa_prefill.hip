@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // ---- tile loads: thread tid moves 32 bytes (2 chunks) of K and of V of tile row tid/8 ----
   // Loads are unconditional (a row outside the keys reads a valid dummy row and is
   // zeroed when written to LDS).  Block ids are read one tile ahead of their use.
-  const int lrow = tid >> 3, lc0 = (tid & 7) * 2;
+  const int lrow = tid >> 3, lc = tid & 7;  // chunks lc and lc + 8 of row lrow
   const size_t hstride = (size_t)kBlockSize * kD;  // elements per (block, head)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
@@ -225,19 +225,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     const size_t off = row_source(t, blk, pre, ok_k);
     const uint16_t* src = (pre ? kc : knew) + off;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc0 + i));
+    for (int i = 0; i < 2; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
   };
   auto load_v = [&](int t, int blk) {
     bool pre;
     const size_t off = row_source(t, blk, pre, ok_v);
     const uint16_t* src = (pre ? vc : vnew) + off;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc0 + i));
+    for (int i = 0; i < 2; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
   };
   auto store_rows = [&](u32x4* dst, int stride, const u32x4 (&r)[2], bool ok) {
     const u32x4 z = {0u, 0u, 0u, 0u};  // zero: tail rows, prefix rows with a bad block id
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[lrow * stride + lc0 + i] = ok ? r[i] : z;
+    for (int i = 0; i < 2; ++i) dst[lrow * stride + lc + 8 * i] = ok ? r[i] : z;
   };
 
   {
