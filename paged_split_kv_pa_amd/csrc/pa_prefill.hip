@@ -22,8 +22,7 @@
 //
 // Per 64-key tile: K and V rows are loaded from the cache (key < c, through the
 // block table) or from the packed new tokens (c <= key < c + L), into padded LDS rows.
-//   S^T = K Q^T:   v_mfma_f32_16x16x32, A = 16 keys x 32 dims, B = Q (both from LDS,
-//                  where the work-group's 256 query rows are staged once):
+//   S^T = K Q^T:   v_mfma_f32_16x16x32, A = 16 keys x 32 dims (LDS), B = Q (registers):
 //                  lane (r16, kg) gets keys 4kg..4kg+3 of query row r16.
 //   online softmax per query row in base 2 (scale * log2 e folded in), causal mask on
 //                  the tiles that reach the row's own position, lazy rescale as in decode.
@@ -113,19 +112,18 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// LDS rows of K, V and Q are padded to 288 bytes, which leaves all three operand reads
-// free of bank conflicts with plain linear addresses (measured with the LDS bank-conflict
-// counter: the 16-byte reads of 16 rows per K / Q operand, and the 8-byte transposing
-// reads of 8 rows per half-wave for V; a 256-byte row conflicts 28 cycles per read, a
+// LDS rows of K and V are padded to 288 bytes, which leaves both operand reads free of
+// bank conflicts with plain linear addresses (measured with the LDS bank-conflict
+// counter: the 16-byte reads of 16 rows per K operand, and the 8-byte transposing reads
+// of 8 rows per half-wave for V; a 256-byte row conflicts 28 cycles per K read, a
 // 272-byte row 4).
-constexpr int kKRow = kChunks + 2;  // K and Q row stride in 16-byte units
+constexpr int kKRow = kChunks + 2;  // K row stride in 16-byte units
 constexpr int kVRow = kChunks + 2;  // V row stride in 16-byte units
 
 template <int DT, int G>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
   constexpr int kPos = kRows / G;  // query positions per work-group
-  __shared__ u32x4 s_q[kRows * kKRow];
   __shared__ u32x4 s_k[2][kTile * kKRow];
   __shared__ u32x4 s_v[2][kTile * kVRow];
 
@@ -151,31 +149,31 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   const int nkeys = c + pend;
   const int ntiles = (nkeys + kTile - 1) / kTile;
 
-  // ---- queries in LDS (rows of 288 bytes, like K), per-row state ----
-  // Thread tid copies 64 bytes (4 chunks) of work-group row tid / 2; a negative scale is
-  // carried by flipping the sign of q (exact in 16-bit floats), since the softmax works
-  // on raw dot products scaled by |scale| log2(e): max(scale * s) is |scale| * max of the
-  // flipped products.  Rows past the last position are zero.
+  // ---- query operands and per-row state ----
+  // Column group cg of this wave: rows 32w + 16cg + (0..15); lane column r16.  The
+  // softmax works on raw dot products scaled by |scale| log2(e); a negative scale is
+  // carried by flipping the sign of q (exact in 16-bit floats), so max(scale * s) is
+  // |scale| * max of the flipped products.
+  u32x4 qf[2][4];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
+  int qpos_col[2];
   {
-    const int row = tid >> 1, c0 = (tid & 1) * 8;
-    const int pos = p0 + row / G;
-    const int hq = g * G + row % G;
-    const bool valid = pos < L;
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * kD;
     const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * (c0 + i)) : u32x4{0u, 0u, 0u, 0u};
-      s_q[row * kKRow + c0 + i] = v ^ u32x4{flip, flip, flip, flip};
+    for (int cg = 0; cg < 2; ++cg) {
+      const int row = 32 * w + 16 * cg + r16;
+      const int pos = p0 + row / G;
+      const int hq = g * G + row % G;
+      qpos_col[cg] = pos;
+      const bool valid = pos < L;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                             ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * kD;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qf[cg][kk] = (valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
+                            : u32x4{0u, 0u, 0u, 0u}) ^ u32x4{flip, flip, flip, flip};
     }
   }
   const float sl = fabsf(a.scale_log2);
-  int qpos_col[2];  // position of query row r16 of column group cg
-#pragma unroll
-  for (int cg = 0; cg < 2; ++cg) qpos_col[cg] = p0 + (32 * w + 16 * cg + r16) / G;
-  // Q operand of column group cg, k step kk: Q[row 32w + 16cg + r16][32kk + 8kg .. +7].
-  const u32x4* qbase = s_q + (32 * w + r16) * kKRow + kg;
   f32x4 O[2][8];
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg)
@@ -260,11 +258,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // S^T of tile t.
   auto qk = [&](int t) {
     const u32x4* kb = s_k[t & 1];
-    u32x4 qv[2][4], ka[4][4];
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qv[cg][kk] = qbase[16 * cg * kKRow + 4 * kk];
+    u32x4 ka[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -275,10 +269,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
       for (int cg = 0; cg < 2; ++cg) {
         S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) S[rb][cg] = mfma32<kBF>(ka[rb][kk], qv[cg][kk], S[rb][cg]);
+        for (int kk = 0; kk < 4; ++kk) S[rb][cg] = mfma32<kBF>(ka[rb][kk], qf[cg][kk], S[rb][cg]);
       }
     // the reads of the next row block's K run under the current row block's products
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int rb = 0; rb < 3; ++rb) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
