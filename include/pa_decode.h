@@ -312,7 +312,7 @@ pa_status_t pa_copy_blocks_profiled(void* k_cache, void* v_cache, int64_t block_
  * Paged prefix-prefill attention.  Source: project_6
  * optimizations/prefix_prefill_patch.py (commit fee8f1b), docstring: the
  * prefix_prefill kernel, Flash-Attention style over query tiles and K/V tiles,
- * fp16/bf16, head_dim 128, GQA; and the "Dockerfile" commit page (project_6 commit
+ * fp16/bf16, head_dim 128 (256 less often), GQA; and the "Dockerfile" commit page (project_6 commit
  * 96f4baf), "What CAN be optimized", items 1-2 (the same kernel; prefill chunks).
  * What it computes (the plainest reading of the pages): sequence b has a prefix of
  * c_b = context_lens[b] tokens in the paged cache (block_tables as in decode) and a
@@ -322,7 +322,7 @@ pa_status_t pa_copy_blocks_profiled(void* k_cache, void* v_cache, int64_t block_
  *   out[query_start[b] + i, h, :] = sum_j softmax_j(scale * <q, k_j>) v_j.
  * The new tokens' K/V are read from k_new / v_new only (writing them into the cache
  * is a separate step).  Layouts and dtypes as in decode; out [T, Hq, D] in q's dtype.
- * Built: fp16 and bf16, head_dim 128, block_size 16, Hq/Hkv in {1, 2, 4, 8, 16}
+ * Built: fp16 and bf16, head_dim 128 and 256, block_size 16, Hq/Hkv in {1, 2, 4, 8, 16}
  * (others: PA_ERR_UNSUPPORTED).  query_start must be non-decreasing from 0 with
  * query_start[S] <= T (rows past T are not read or written); a context length is
  * clamped to MB*16.  max_query_len bounds every L_b and sizes the grid (<= 0: T);

@@ -432,8 +432,9 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
                 d->num_tokens);
   if (d->dtype == PA_F32)
     return fail(PA_ERR_UNSUPPORTED, "prefill is built for fp16 and bf16 (matrix cores)");
-  if (d->head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)", d->head_dim);
+  if (d->head_dim != 128 && d->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "prefill is built for head_dim 128 and 256 (got %d)",
+                d->head_dim);
   if (d->block_size != pa::kBlockSize)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", d->block_size);
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -472,7 +473,7 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   a.Hkv = d->num_kv_heads;
   a.NB = d->num_blocks;
   a.MB = d->max_blocks_per_seq;
-  return hip_status(pa::launch_prefill(d->dtype, G, a, d->num_seqs, maxq,
+  return hip_status(pa::launch_prefill(d->dtype, G, d->head_dim, a, d->num_seqs, maxq,
                                        static_cast<hipStream_t>(stream), e0, e1),
                     "prefill launch");
 }

@@ -97,11 +97,11 @@ hipError_t launch_copy_blocks(const CopyArgs& a, long long num_pairs, bool with_
 
 // ---- paged prefix prefill (pa_prefill.hip) ---------------------------------------------
 struct PrefillArgs {
-  void* out;                 // [T, Hq, 128]
-  const void* q;             // [T, Hq, 128]
-  const void* k_new;         // [T, Hkv, 128]
-  const void* v_new;         // [T, Hkv, 128]
-  const void* k_cache;       // [NB, Hkv, 16, 128]
+  void* out;                 // [T, Hq, D]
+  const void* q;             // [T, Hq, D]
+  const void* k_new;         // [T, Hkv, D]
+  const void* v_new;         // [T, Hkv, D]
+  const void* k_cache;       // [NB, Hkv, 16, D]
   const void* v_cache;
   const int32_t* bt;         // [S, MB]
   const int32_t* ctx;        // [S] prefix lengths
@@ -109,10 +109,9 @@ struct PrefillArgs {
   float scale_log2;          // scale * log2(e)
   int32_t T, Hq, Hkv, NB, MB;
 };
-int prefill_positions_per_workgroup(int group);
-// Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128, fp16/bf16.
-// e0 / e1 (may be null) are recorded when the kernel starts / ends.
-hipError_t launch_prefill(int dtype, int group, const PrefillArgs& a, int num_seqs,
+// Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128 or 256,
+// fp16/bf16.  e0 / e1 (may be null) are recorded when the kernel starts / ends.
+hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& a, int num_seqs,
                           int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1);
 
 }  // namespace pa

@@ -3,15 +3,16 @@
 // Source: project_6 optimizations/prefix_prefill_patch.py (commit fee8f1b), docstring:
 // the prefix_prefill kernel is Flash-Attention style -- a grid of (batch, heads,
 // query tiles of BLOCK_M positions), K/V tiles of BLOCK_N tokens staged in on-chip
-// memory, fp16/bf16, head_dim 128, GQA.  What it computes (the reading stated with the
+// memory, fp16/bf16, head_dim 128 (256 less often), GQA.  What it computes (the reading stated with the
 // oracle): new token i of sequence b (absolute position c_b + i) attends to the c_b
 // prefix tokens in the paged cache and to new tokens 0..i, whose K/V arrive packed.
 //
-// Work-group: 8 waves, 256 query rows of one KV head g of one sequence: positions
-// [p0, p0 + 256/G) x the G query heads of g, row r = (position p0 + r / G, head
-// g*G + r % G).  Sharing every K/V tile among the G heads and 256/G positions is what
-// makes the tile traffic small next to the MFMA work.  Wave w owns rows 32w..32w+31,
-// as two column groups of 16 rows (the MFMA's 16 columns).
+// Work-group: 8 waves, R query rows of one KV head g of one sequence (R = 256 at head_dim
+// 128, 128 at 256): positions [p0, p0 + R/G) x the G query heads of g, row r = (position
+// p0 + r / G, head g*G + r % G).  Sharing every K/V tile among the G heads and R/G
+// positions is what makes the tile traffic small next to the MFMA work.  Wave w owns
+// R/8 rows, as column groups of 16 rows (the MFMA's 16 columns): two at head_dim 128,
+// one at 256.
 //
 // Two waves share each SIMD, and they take turns: the work of a wave alternates between
 // a matrix phase (O += P V for the previous tile, then S^T = K Q^T for this one) and a
@@ -52,11 +53,22 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;
-constexpr int kD = 128;          // head_dim built
-constexpr int kRows = 256;       // query rows per work-group
-constexpr int kThreads = 512;    // 8 waves of 32 rows
-constexpr int kTile = 64;        // keys per K/V tile
-constexpr int kChunks = kD / 8;  // 16-byte chunks per row
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kTile = 64;      // keys per K/V tile
+
+// Work-group shape for head_dim D.  A wave owns CG column groups of 16 query rows: two at
+// D = 128, one at D = 256, where the output accumulators of 16 rows already take 64
+// registers per lane (two waves per SIMD leave 256 per lane).
+template <int D>
+struct Shape {
+  static constexpr int CG = D == 128 ? 2 : 1;  // 16-row column groups per wave
+  static constexpr int ROWS = 8 * 16 * CG;     // query rows per work-group
+  static constexpr int KK = D / 32;            // k steps of QK^T
+  static constexpr int JD = D / 16;            // 16-column blocks of O
+  static constexpr int CH = D / 8;             // 16-byte chunks per K / V row
+  static constexpr int ROW = CH + 2;           // LDS row stride, 16-byte units
+  static constexpr int XC = CH / 8;            // chunks of a row one thread stages
+};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -112,20 +124,20 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// LDS rows of K and V are padded to 288 bytes, which leaves both operand reads free of
-// bank conflicts with plain linear addresses (measured with the LDS bank-conflict
-// counter: the 16-byte reads of 16 rows per K operand, and the 8-byte transposing reads
-// of 8 rows per half-wave for V; a 256-byte row conflicts 28 cycles per K read, a
-// 272-byte row 4).
-constexpr int kKRow = kChunks + 2;  // K row stride in 16-byte units
-constexpr int kVRow = kChunks + 2;  // V row stride in 16-byte units
+// LDS rows of K and V are padded by 32 bytes (288 bytes at head_dim 128, 544 at 256): a
+// row stride of 32 bytes modulo 256 leaves both operand reads free of bank conflicts with
+// plain linear addresses (measured with the LDS bank-conflict counter: the 16-byte reads
+// of 16 rows per K operand, and the 8-byte transposing reads of 8 rows per half-wave for
+// V; a 256-byte row conflicts 28 cycles per K read, a 272-byte row 4).
 
-template <int DT, int G>
+template <int DT, int G, int D>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
-  constexpr int kPos = kRows / G;  // query positions per work-group
-  __shared__ u32x4 s_k[2][kTile * kKRow];
-  __shared__ u32x4 s_v[2][kTile * kVRow];
+  using Sh = Shape<D>;
+  constexpr int CG = Sh::CG, KK = Sh::KK, JD = Sh::JD, ROW = Sh::ROW, XC = Sh::XC;
+  constexpr int kPos = Sh::ROWS / G;  // query positions per work-group
+  __shared__ u32x4 s_k[2][kTile * ROW];
+  __shared__ u32x4 s_v[2][kTile * ROW];
 
   const int g = blockIdx.y, b = blockIdx.z;
   const int p0 = blockIdx.x * kPos;
@@ -150,53 +162,53 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   const int ntiles = (nkeys + kTile - 1) / kTile;
 
   // ---- query operands and per-row state ----
-  // Column group cg of this wave: rows 32w + 16cg + (0..15); lane column r16.  The
+  // Column group cg of this wave: rows 16 CG w + 16cg + (0..15); lane column r16.  The
   // softmax works on raw dot products scaled by |scale| log2(e); a negative scale is
   // carried by flipping the sign of q (exact in 16-bit floats), so max(scale * s) is
   // |scale| * max of the flipped products.
-  u32x4 qf[2][4];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
-  int qpos_col[2];
+  u32x4 qf[CG][KK];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
+  int qpos_col[CG];
   {
     const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      const int row = 32 * w + 16 * cg + r16;
+    for (int cg = 0; cg < CG; ++cg) {
+      const int row = 16 * CG * w + 16 * cg + r16;
       const int pos = p0 + row / G;
       const int hq = g * G + row % G;
       qpos_col[cg] = pos;
       const bool valid = pos < L;
       const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                             ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * kD;
+                             ((size_t)(r0 + (valid ? pos : 0)) * a.Hq + hq) * D;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
         qf[cg][kk] = (valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
                             : u32x4{0u, 0u, 0u, 0u}) ^ u32x4{flip, flip, flip, flip};
     }
   }
   const float sl = fabsf(a.scale_log2);
-  f32x4 O[2][8];
+  f32x4 O[CG][JD];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg)
+  for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JD; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Row sums of P come from the matrix cores too: one more PV product per column group
   // with an all-ones B operand leaves sum_k P[row][k] in every column, in the same
   // row layout as O (and from the same bf16-rounded P as O).
-  f32x4 Lacc[2];
-  float m_ref[2];
+  f32x4 Lacc[CG];
+  float m_ref[CG];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
+  for (int cg = 0; cg < CG; ++cg) {
     m_ref[cg] = kNegInf;
     Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint32_t one2 = kBF ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0
   const u32x4 ones = {one2, one2, one2, one2};
 
-  // ---- tile loads: thread tid moves 32 bytes (2 chunks) of K and of V of tile row tid/8 ----
+  // ---- tile loads: thread tid moves XC chunks (lc, lc + 8, ...) of K and of V of tile row tid/8 ----
   // Loads are unconditional (a row outside the keys reads a valid dummy row and is
   // zeroed when written to LDS).  Block ids are read one tile ahead of their use.
-  const int lrow = tid >> 3, lc = tid & 7;  // chunks lc and lc + 8 of row lrow
-  const size_t hstride = (size_t)kBlockSize * kD;  // elements per (block, head)
+  const int lrow = tid >> 3, lc = tid & 7;  // chunks lc + 8 i of row lrow
+  const size_t hstride = (size_t)kBlockSize * D;  // elements per (block, head)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
   const uint16_t* knew = static_cast<const uint16_t*>(a.k_new);
@@ -213,37 +225,37 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     pre = key < c && (unsigned)blk < (unsigned)a.NB;
     const bool fresh = key >= c && key < nkeys;
     ok = pre || fresh;
-    return pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * kD
-               : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * kD : (size_t)r0 * a.Hkv * kD);
+    return pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * D
+               : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * D : (size_t)r0 * a.Hkv * D);
   };
-  u32x4 kr[2], vr[2];
+  u32x4 kr[XC], vr[XC];
   bool ok_k = false, ok_v = false;
   auto load_k = [&](int t, int blk) {
     bool pre;
     const size_t off = row_source(t, blk, pre, ok_k);
     const uint16_t* src = (pre ? kc : knew) + off;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
+    for (int i = 0; i < XC; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
   };
   auto load_v = [&](int t, int blk) {
     bool pre;
     const size_t off = row_source(t, blk, pre, ok_v);
     const uint16_t* src = (pre ? vc : vnew) + off;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
+    for (int i = 0; i < XC; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
   };
-  auto store_rows = [&](u32x4* dst, int stride, const u32x4 (&r)[2], bool ok) {
+  auto store_rows = [&](u32x4* dst, const u32x4 (&r)[XC], bool ok) {
     const u32x4 z = {0u, 0u, 0u, 0u};  // zero: tail rows, prefix rows with a bad block id
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[lrow * stride + lc + 8 * i] = ok ? r[i] : z;
+    for (int i = 0; i < XC; ++i) dst[lrow * ROW + lc + 8 * i] = ok ? r[i] : z;
   };
 
   {
     const int blk0 = fetch_block(0);
     load_k(0, blk0);
     load_v(0, blk0);
-    store_rows(s_k[0], kKRow, kr, ok_k);
-    store_rows(s_v[0], kVRow, vr, ok_v);
+    store_rows(s_k[0], kr, ok_k);
+    store_rows(s_v[0], vr, ok_v);
   }
   int blk_k = fetch_block(1), blk_v = blk_k;
   load_k(1, blk_k);
@@ -252,33 +264,35 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   blk_v = blk_k;
   __syncthreads();
 
-  f32x4 S[4][2];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
-  u32x4 P[2][2];  // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1)
+  f32x4 S[4][CG];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
+  u32x4 P[CG][2];  // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1)
 
   // S^T of tile t.
   auto qk = [&](int t) {
     const u32x4* kb = s_k[t & 1];
-    u32x4 ka[4][4];
+    u32x4 ka[KK][4];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) ka[kk][rb] = kb[(16 * rb + r16) * ROW + 4 * kk + kg];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[rb][kk] = kb[(16 * rb + r16) * kKRow + 4 * kk + kg];
+      for (int cg = 0; cg < CG; ++cg) S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
-        S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) S[rb][cg] = mfma32<kBF>(ka[rb][kk], qf[cg][kk], S[rb][cg]);
-      }
-    // the reads of the next row block's K run under the current row block's products
+        for (int cg = 0; cg < CG; ++cg) S[rb][cg] = mfma32<kBF>(ka[kk][rb], qf[cg][kk], S[rb][cg]);
+    // the K reads of the next k step run under the current step's products
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) {
+    for (int kk = 0; kk < KK - 1; ++kk) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
   };
   // O += P V for tile t.  V operand [st][jd]: the 32 keys of step st (in the P k-slot
   // order) x head-dim 16 jd + (0..15); lane (j, kg) reads 8 bytes of key
@@ -286,44 +300,44 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // transposing read hands lane (n, kg) the 4 keys of its k-slots at head-dim 16 jd + n.
   auto pv = [&](int t) {
     const char* vbase = reinterpret_cast<const char*>(s_v[t & 1]);
-    u32x4 vb[2][8];
+    u32x4 vb[2][JD];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
+      for (int jd = 0; jd < JD; ++jd) {
         const int key = 32 * st + 4 * kg + (r16 >> 2);
-        const char* src = vbase + key * (kVRow * 16) + 32 * jd + 8 * (r16 & 3);
+        const char* src = vbase + key * (ROW * 16) + 32 * jd + 8 * (r16 & 3);
         const u32x2 lo = lds_read_tr(src);
-        const u32x2 hi = lds_read_tr(src + 16 * kVRow * 16);
+        const u32x2 hi = lds_read_tr(src + 16 * ROW * 16);
         vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
+      for (int jd = 0; jd < JD; ++jd)
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg) O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
+        for (int cg = 0; cg < CG; ++cg) O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) Lacc[cg] = mfma32<kBF>(P[cg][st], ones, Lacc[cg]);
+      for (int cg = 0; cg < CG; ++cg) Lacc[cg] = mfma32<kBF>(P[cg][st], ones, Lacc[cg]);
     }
-    // V reads run two operands ahead of the products that use them
+    // V reads (two per operand) run four operands ahead of the products that use them
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int k = 0; k < 14; ++k) {
+    for (int k = 0; k < 2 * JD - 4; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, CG, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6 * CG, 0);
   };
   // Softmax of tile t: row max (masked keys become -inf on diagonal tiles, where S then
   // holds scaled logits), the rescale of O when a row max grows past the slack, and P.
   auto softmax = [&](int t) {
     const int kbase = t * kTile;
     const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
-    float bm[2];
+    float bm[CG];
     bool grow = false;
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
+    for (int cg = 0; cg < CG; ++cg) {
       float mx = kNegInf;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -343,7 +357,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     }
     if (__any(grow)) {  // rare
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
+      for (int cg = 0; cg < CG; ++cg) {
         const float m_new = fmaxf(m_ref[cg], bm[cg]);
         const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
         m_ref[cg] = m_new;
@@ -351,7 +365,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < JD; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
 #pragma unroll
@@ -361,7 +375,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
+    for (int cg = 0; cg < CG; ++cg) {
       const float nm = -m_ref[cg];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -387,12 +401,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // rows requested are valid dummy rows): with no branch around them the compiler's wait
   // counts stay exact, and no wait drains the loads still in flight.
   auto io_k = [&](int u) {
-    store_rows(s_k[(u + 1) & 1], kKRow, kr, ok_k);
+    store_rows(s_k[(u + 1) & 1], kr, ok_k);
     load_k(u + 2, blk_k);
     blk_k = fetch_block(u + 3);
   };
   auto io_v = [&](int u) {
-    store_rows(s_v[(u + 1) & 1], kVRow, vr, ok_v);
+    store_rows(s_v[(u + 1) & 1], vr, ok_v);
     load_v(u + 2, blk_v);
     blk_v = fetch_block(u + 3);
   };
@@ -406,8 +420,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     if (t_ >= 1) pv(t_ - 1);                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                 \
     if (t_ < ntiles) qk(t_);                                                           \
-    _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                  \
-      _Pragma("unroll") for (int j = 0; j < 8; ++j) asm("" : "+v"(O[cg][j]));          \
+    _Pragma("unroll") for (int cg = 0; cg < CG; ++cg)                                 \
+      _Pragma("unroll") for (int j = 0; j < JD; ++j) asm("" : "+v"(O[cg][j]));         \
     if (GRP == 0) {                                                                    \
       if (t_ >= 1) io_v(t_ - 1); /* phase 0 has no traffic */                          \
     } else {                                                                           \
@@ -432,18 +446,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
+  for (int cg = 0; cg < CG; ++cg) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float li = Lacc[cg][i];
-      const int row = 32 * w + 16 * cg + 4 * kg + i;
+      const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
       const int pos = p0 + row / G;
       if (pos >= L) continue;
       const int hq = g * G + row % G;
       const float inv = 1.f / li;
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * kD;
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * D;
 #pragma unroll
-      for (int jd = 0; jd < 8; jd += 2) {
+      for (int jd = 0; jd < JD; jd += 2) {
         const uint32_t two = pack2<kBF>(O[cg][jd][i] * inv, O[cg][jd + 1][i] * inv);
         orow[16 * jd + r16] = (uint16_t)two;
         orow[16 * (jd + 1) + r16] = (uint16_t)(two >> 16);
@@ -452,16 +466,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 }
 
-template <int DT>
-hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0,
-                    hipEvent_t e1) {
+template <int DT, int D>
+hipError_t launch_g(int G, const PrefillArgs& a, int num_seqs, int max_query_len,
+                    hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const int per = Shape<D>::ROWS / G;
+  const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
   const dim3 block(kThreads);
   switch (G) {
-    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D>), grid, block, 0, st, e0, e1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -469,15 +485,17 @@ hipError_t launch_g(int G, const PrefillArgs& a, dim3 grid, hipStream_t st, hipE
 
 }  // namespace
 
-int prefill_positions_per_workgroup(int group) { return kRows / group; }
-
-hipError_t launch_prefill(int dtype, int group, const PrefillArgs& a, int num_seqs,
+hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& a, int num_seqs,
                           int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-  const int per = kRows / group;
-  const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
-  return dtype == PA_BF16 ? launch_g<PA_BF16>(group, a, grid, stream, e0, e1)
-       : dtype == PA_F16  ? launch_g<PA_F16>(group, a, grid, stream, e0, e1)
-                          : hipErrorInvalidValue;
+  if (head_dim == 128)
+    return dtype == PA_BF16 ? launch_g<PA_BF16, 128>(group, a, num_seqs, max_query_len, stream, e0, e1)
+         : dtype == PA_F16  ? launch_g<PA_F16, 128>(group, a, num_seqs, max_query_len, stream, e0, e1)
+                            : hipErrorInvalidValue;
+  if (head_dim == 256)
+    return dtype == PA_BF16 ? launch_g<PA_BF16, 256>(group, a, num_seqs, max_query_len, stream, e0, e1)
+         : dtype == PA_F16  ? launch_g<PA_F16, 256>(group, a, num_seqs, max_query_len, stream, e0, e1)
+                            : hipErrorInvalidValue;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

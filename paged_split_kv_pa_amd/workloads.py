@@ -355,8 +355,17 @@ def _pf_batch(seed=12):
                                  num_kv_heads=4, head_dim=128, dtype="f16")
 
 
-PREFILL_CONFIGS = {0: _pf_small, 1: _pf_chunk, 2: _pf_batch}
-PREFILL_CONFIG_NAMES = {0: "pf_small", 1: "pf_chunk_8k_at_64k", 2: "pf_batch_mixed"}
+def _pf_d256(seed=13):
+    # head_dim 256 (the pages' rarer head size, as in the mixed decode workload): a
+    # 4096-token chunk after a 16384-token prefix, 16/2 heads, fp16, values N(0, 0.5^2).
+    return make_prefill_workload("pf_chunk_4k_at_16k_d256", seed, context_lens=[16384],
+                                 query_lens=[4096], num_q_heads=16, num_kv_heads=2,
+                                 head_dim=256, dtype="f16", sigma=0.5)
+
+
+PREFILL_CONFIGS = {0: _pf_small, 1: _pf_chunk, 2: _pf_batch, 3: _pf_d256}
+PREFILL_CONFIG_NAMES = {0: "pf_small", 1: "pf_chunk_8k_at_64k", 2: "pf_batch_mixed",
+                        3: "pf_chunk_4k_at_16k_d256"}
 
 
 def prefill_config(i):

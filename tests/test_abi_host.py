@@ -380,7 +380,8 @@ PF_FAKE = [ctypes.c_void_p(0x20000 + 0x1000 * i) for i in range(9)]
     (dict(num_blocks=0), -3),
     (dict(max_query_len=101), -3),
     (dict(dtype=B.PA_F32), -6),
-    (dict(head_dim=256), -6),
+    (dict(head_dim=64), -6),
+    (dict(head_dim=192), -6),
     (dict(block_size=32), -6),
     (dict(num_q_heads=96, num_kv_heads=4), -6),   # G = 24
     (dict(num_kv_heads=70000, num_q_heads=70000), -6),
