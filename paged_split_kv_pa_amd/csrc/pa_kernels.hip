@@ -191,20 +191,28 @@ struct Part {
   int nblk;    // cache blocks in the range
 };
 
-__device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it) {
+// The token range this work-group covers when its partition is full: first token and
+// length.  It depends on the grid item only, not on the context length.
+__device__ __forceinline__ void nominal_range(const AttnArgs& a, const Item& it, int& tok0,
+                                              int& len) {
+  len = a.P;
+  tok0 = it.p * a.P;
+  if (it.piece >= 0) {
+    len = a.P >> a.split.shift;
+    tok0 += it.piece * len;
+  }
+}
+
+// n: the sequence's context length as read from context_lens.
+__device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it, int n) {
   Part r;
-  int n = a.ctx[it.b];
   const int cap = a.MB * kBlockSize;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int np = (n + a.P - 1) / a.P;
   r.n = n;
   r.nparts = np > a.Pmax ? a.Pmax : np;
-  int len = a.P;
-  r.tok0 = it.p * a.P;
-  if (it.piece >= 0) {
-    len = a.P >> a.split.shift;
-    r.tok0 += it.piece * len;
-  }
+  int len;
+  nominal_range(a, it, r.tok0, len);
   r.ntok = min(len, n - r.tok0);
   r.nblk = (r.ntok + kBlockSize - 1) / kBlockSize;
   return r;
@@ -284,27 +292,45 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
   const int r16 = lane & 15;  // token row (K loads), head column (Q, S), V column run
   const int kg = lane >> 4;   // k-group of the MFMA operands
 
-  const Part pt = plan_partition(a, it);
+  // The block ids of the range a full partition would cover (clipped to the table
+  // width, which bounds every context) and the queries do not depend on the context
+  // length: they are requested in the same memory round trip as that length, so the
+  // first K/V loads wait for one cold round trip, not two.  Entries past the context
+  // are fetched but never used as addresses.
+  const int n_ctx = a.ctx[b];
+  int tok0n, lenn;
+  nominal_range(a, it, tok0n, lenn);
+  const int blk0 = tok0n / kBlockSize;
+  const int nblk_nom = min(lenn / kBlockSize, a.MB - blk0);
+  const int kcount_nom = w < nblk_nom ? (nblk_nom - w + NW - 1) / NW : 0;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB + blk0;
+  int btv = lane < min(64, kcount_nom) ? btrow[w + NW * lane] : 0;  // first 64 block ids
+
+  // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
+  // pad the group to 16 heads).  Kept in LDS in lane order: conflict-free 16-byte reads.
+  // The loads are unconditional (padding lanes read the group's last head and store
+  // zeros) and the LDS store comes before any use of the context length, so the
+  // compiler can neither sink them behind it nor make its load wait for them.
+  if (w == 0) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((size_t)b * a.Hq + (size_t)g * G + min(r16, G - 1)) * D;
+    u32x4 qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s_qf[kk][lane] = r16 < G ? qf[kk] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const Part pt = plan_partition(a, it, n_ctx);
   if (it.p >= pt.nparts) {
     if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
     return;
   }
   if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
+  // pt.nblk <= nblk_nom: the context never extends past the table, so every block id
+  // used below is among those fetched above.
   const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
-  const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
-
-  int btv = lane < min(64, kcount) ? btrow[w + NW * lane] : 0;  // first 64 block ids
-
-  // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
-  // pad the group to 16 heads).  Kept in LDS in lane order: conflict-free 16-byte reads.
-  if (w == 0) {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * G + r16) * D;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      s_qf[kk][lane] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
-                               : u32x4{0u, 0u, 0u, 0u};
-  }
 
   const size_t hstride = (size_t)kBlockSize * D;
   const size_t bstride = (size_t)a.Hkv * hstride;
@@ -595,7 +621,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   const int lane = tid & 63;
   const int t = lane >> 2, r = lane & 3;
 
-  const Part pt = plan_partition(a, it);
+  const Part pt = plan_partition(a, it, a.ctx[b]);
   if (it.p >= pt.nparts) {
     if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
     return;
