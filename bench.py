@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0,
                     help="KV pool replicas rotated across steps (0 = enough for >= 1 GiB)")
     ap.add_argument("--variant", type=int, default=-1, help="matrix-core kernel variant")
+    ap.add_argument("--split-pieces", type=int, default=-1,
+                    help="work split: -1 automatic, 0 off, 2/4/8/16 pieces per item from "
+                         "--split-first on")
+    ap.add_argument("--split-first", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the attention kernel's start/stop events on every N-th "
                          "timed step (the events cost a little GPU time per step)")
@@ -502,6 +506,8 @@ def main():
     torch.cuda.set_device(0)
     if args.variant >= 0:
         B.pa_set_mfma_variant(args.variant)
+    if args.split_pieces != -1:
+        B.pa_set_work_split(args.split_pieces, args.split_first)
 
     log(f"generating workload {wl.CONFIG_NAMES[args.config]}")
     w = wl.config(args.config)
@@ -622,6 +628,7 @@ def main():
             "path": "v1" if path == B.PA_PATH_V1 else "v2",
             "kv_bytes_per_step": kvb, "kv_pool_copies": R,
             "mfma_variant": B.pa_get_mfma_variant(),
+            "work_split": list(B.pa_get_work_split()),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

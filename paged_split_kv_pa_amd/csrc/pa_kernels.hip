@@ -318,6 +318,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg);
+    asm volatile("" ::"s"(n_ctx));  // see attn_valu_kernel
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s_qf[kk][lane] = r16 < G ? qf[kk] : u32x4{0u, 0u, 0u, 0u};
   }
@@ -621,25 +622,44 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   const int lane = tid & 63;
   const int t = lane >> 2, r = lane & 3;
 
-  const Part pt = plan_partition(a, it, a.ctx[b]);
+  // Context length, the first 64 block ids of the nominal range and the queries in one
+  // memory round trip (see attn_mfma_kernel).
+  const int n_ctx = a.ctx[b];
+  int tok0n, lenn;
+  nominal_range(a, it, tok0n, lenn);
+  const int blk0 = tok0n / kBlockSize;
+  const int nblk_nom = min(lenn / kBlockSize, a.MB - blk0);
+  const int kcount_nom = w < nblk_nom ? (nblk_nom - w + kWaves - 1) / kWaves : 0;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB + blk0;
+  int btv = lane < min(64, kcount_nom) ? btrow[w + kWaves * lane] : 0;
+
+  // Stage the head group's queries, pre-multiplied by scale*log2(e), as fp32 (all loads
+  // issued before the first store).
+  constexpr int kQIter = (G * D + kThreads - 1) / kThreads;
+  float qv[kQIter];
+#pragma unroll
+  for (int i = 0; i < kQIter; ++i) {
+    const int idx = min(tid + i * kThreads, G * D - 1);
+    const size_t src = ((size_t)b * a.Hq + (size_t)g * G) * D + idx;
+    if constexpr (DT == PA_F32) qv[i] = static_cast<const float*>(a.q)[src];
+    else qv[i] = half_lo<DT>(static_cast<const uint16_t*>(a.q)[src]);
+  }
+  // The context length is consumed here, so its load is issued before the wait for the
+  // query loads (the scheduler placed it after that wait otherwise).
+  asm volatile("" ::"s"(n_ctx));
+#pragma unroll
+  for (int i = 0; i < kQIter; ++i)
+    if (tid + i * kThreads < G * D) s_q[tid + i * kThreads] = qv[i] * a.scale_log2;
+
+  const Part pt = plan_partition(a, it, n_ctx);
   if (it.p >= pt.nparts) {
     if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
     return;
   }
   if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
+  // pt.nblk <= nblk_nom, so the first chunk's block ids are all in btv.
   const int kcount = w < pt.nblk ? (pt.nblk - w + kWaves - 1) / kWaves : 0;
-  const int32_t* btrow = a.bt + (size_t)b * a.MB + pt.tok0 / kBlockSize;
-
-  // Stage the head group's queries, pre-multiplied by scale*log2(e), as fp32.
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const size_t src = ((size_t)b * a.Hq + (size_t)g * G) * D + idx;
-    float qv;
-    if constexpr (DT == PA_F32) qv = static_cast<const float*>(a.q)[src];
-    else qv = half_lo<DT>(static_cast<const uint16_t*>(a.q)[src]);
-    s_q[idx] = qv * a.scale_log2;
-  }
-
-  int btv = 0;
+  asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
   const size_t hstride = (size_t)kBlockSize * ROWB;   // bytes per (block, head)
   const size_t bstride = (size_t)a.Hkv * hstride;
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + (size_t)g * hstride;
@@ -752,8 +772,10 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   // and the prefetch overlaps the FMAs.
   for (int c0 = 0; c0 < kcount; c0 += 64) {
     const int cnt = min(64, kcount - c0);
-    btv = lane < cnt ? btrow[w + kWaves * (c0 + lane)] : 0;
-    asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
+    if (c0 > 0) {
+      btv = lane < cnt ? btrow[w + kWaves * (c0 + lane)] : 0;
+      asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
+    }
     const int last = cnt - 1;
     load_block(kA, vA, 0, true);
     for (int k = 0; k < cnt; k += 2) {
