@@ -218,6 +218,34 @@ def test_nan_poison_outside_context_is_never_read(dtype, G, D):
         assert torch.equal(got, clean[path])
 
 
+@pytest.mark.parametrize("dtype,G,D", [("bf16", 8, 128), ("f16", 8, 256), ("f32", 4, 128),
+                                       ("bf16", 2, 128)])
+def test_table_entries_past_the_context_are_never_dereferenced(dtype, G, D):
+    """Block ids past each sequence's last block are fetched ahead of the context length
+    but must never select a block: out-of-range ids there leave the output unchanged."""
+    ctx = [1000, 17, 530, 1, 0, 520]
+    w = small_workload(13, ctx, Hq=2 * G, Hkv=2, D=D, dtype=dtype, pool_factor=1.5)
+    dev = upload(w)
+    bt = w.block_tables.copy()
+    junk = np.array([-1, 2**31 - 1, w.num_blocks, -2**31, 7 * w.num_blocks + 3], np.int32)
+    for b, n in enumerate(ctx):
+        nb = -(-n // 16)
+        tail = bt.shape[1] - nb
+        bt[b, nb:] = junk[np.arange(tail) % len(junk)]
+    devj = dict(dev)
+    devj["block_tables"] = torch.from_numpy(bt).to("cuda")
+    for path, P in ((B.PA_PATH_V1, 512), (B.PA_PATH_V2, 512), (B.PA_PATH_V2, 64)):
+        say(f"table junk dtype={dtype} G={G} D={D} path={path} P={P}")
+        clean = run_path(w, dev, path, P)
+        got = run_path(w, devj, path, P)
+        assert torch.equal(got, clean)
+    say(f"table junk dtype={dtype} G={G} D={D} split into 8 pieces")
+    with work_split(8):
+        clean = run_path(w, dev, B.PA_PATH_V2, 512)
+        got = run_path(w, devj, B.PA_PATH_V2, 512)
+    assert torch.equal(got, clean)
+
+
 def test_identity_coded_values_select_exact_rows():
     """fp32 V = physical_block*16 + slot, q = 0: out is the mean of the selected codes."""
     ctx = [1000, 333, 16, 1]
