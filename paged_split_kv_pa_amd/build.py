@@ -30,7 +30,10 @@ HIPCC_FLAGS = [
 # Per-source flags.  The prefill kernel keeps its 128 output accumulators per lane in
 # VGPRs (the softmax rescales them with VALU instructions); in the default AGPR form the
 # compiler copied them between the register files on every K/V tile.
-SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The decode kernels take their latency-critical arguments as leading scalars (see
+# PA_ATTN_LEAD_PARAMS in pa_kernels.hip); the hardware preloads those into registers.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def hipcc():

@@ -154,6 +154,47 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// ---- leading kernel arguments ---------------------------------------------------------
+// The attention kernels take, ahead of AttnArgs, copies of the fields that a work-group's
+// first memory round trip depends on (the context-length, block-id and query addresses
+// and the integers of the grid mapping).  pa_kernels.hip is built with kernel-argument
+// preloading (gfx950): the hardware places these leading scalar arguments in scalar
+// registers at wave launch, so a work-group issues those loads without first waiting for
+// a load of its argument block.  A by-value struct argument is never preloaded.
+#define PA_ATTN_LEAD_PARAMS                                                                \
+  const int32_t *lead_ctx, const int32_t *lead_bt, const void *lead_q, int32_t lead_Pmax, \
+      int32_t lead_Hkv, int32_t lead_MB, int32_t lead_P, int32_t lead_Hq,                 \
+      int32_t lead_shift, int32_t lead_first
+
+__device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, const int32_t* bt,
+                                              const void* q, int32_t Pmax, int32_t Hkv,
+                                              int32_t MB, int32_t P, int32_t Hq, int32_t shift,
+                                              int32_t first) {
+  a.ctx = ctx;
+  a.bt = bt;
+  a.q = q;
+  a.Pmax = Pmax;
+  a.Hkv = Hkv;
+  a.MB = MB;
+  a.P = P;
+  a.Hq = Hq;
+  a.split.shift = shift;
+  a.split.first = first;
+  return a;
+}
+#define PA_ATTN_APPLY_LEAD(args)                                                        \
+  with_lead(args, lead_ctx, lead_bt, lead_q, lead_Pmax, lead_Hkv, lead_MB, lead_P, lead_Hq, \
+            lead_shift, lead_first)
+
+// Consumes the context length and one field of each 64-byte line of the argument
+// struct (output, K/V bases, pool size and scale), so that their scalar loads are issued
+// before the wait for the first memory round trip and complete within it.  Otherwise
+// the scheduler issued the context-length load after the query waits, and each struct
+// field load only where the field is first used, every one a separate wait.
+#define PA_PIN_EARLY_SCALARS(a, n_ctx)                                                   \
+  asm volatile("" ::"s"(n_ctx), "s"((a).out), "s"((a).k), "s"((a).v), "s"((a).NB),       \
+               "s"((a).scale_log2))
+
 // ---- work-group set-up shared by both attention kernels ------------------------------
 // The grid item of this work-group (see Split): partition p of KV head g of sequence b,
 // whole (piece < 0) or one of its pieces.
@@ -258,7 +299,9 @@ __device__ __forceinline__ void write_zero_group(const AttnArgs& a, int b, int g
 // one wave per SIMD.
 // =======================================================================================
 template <int DT, int D, int G, int NW, int NBUF>
-__global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
+    attn_mfma_kernel(PA_ATTN_LEAD_PARAMS, const AttnArgs args) {
+  const AttnArgs a = PA_ATTN_APPLY_LEAD(args);
   static_assert(DT == PA_BF16 || DT == PA_F16, "matrix-core path is 16-bit only");
   static_assert(G >= 1 && G <= 16, "head group must fit the 16 MFMA columns");
   static_assert(NBUF >= 2, "need at least one block in flight");
@@ -308,17 +351,17 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1) attn_mfma_kernel(co
 
   // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
   // pad the group to 16 heads).  Kept in LDS in lane order: conflict-free 16-byte reads.
-  // The loads are unconditional (padding lanes read the group's last head and store
-  // zeros) and the LDS store comes before any use of the context length, so the
-  // compiler can neither sink them behind it nor make its load wait for them.
-  if (w == 0) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((size_t)b * a.Hq + (size_t)g * G + min(r16, G - 1)) * D;
-    u32x4 qf[NKK];
+  // The loads are unconditional (every wave loads, padding lanes read the group's last
+  // head; wave 0 stores, zeros for the padding) so that the prologue is straight-line and
+  // the compiler can neither sink them behind the context-length test nor put a wait
+  // ahead of them.
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.Hq + (size_t)g * G + min(r16, G - 1)) * D;
+  u32x4 qf[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg);
-    asm volatile("" ::"s"(n_ctx));  // see attn_valu_kernel
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg);
+  PA_PIN_EARLY_SCALARS(a, n_ctx);
+  if (w == 0) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s_qf[kk][lane] = r16 < G ? qf[kk] : u32x4{0u, 0u, 0u, 0u};
   }
@@ -595,7 +638,9 @@ __device__ __forceinline__ float elem(const V& v, int e) {
 }
 
 template <int DT, int D, int G>
-__global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS,
+                                                              const AttnArgs args) {
+  const AttnArgs a = PA_ATTN_APPLY_LEAD(args);
   constexpr int ES = DT == PA_F32 ? 4 : 2;
   constexpr int ROWB = D * ES;   // bytes per cache row
   constexpr int KCH = ROWB / 64; // 16-byte K chunks per lane (a row is split over 4 lanes)
@@ -644,9 +689,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
     if constexpr (DT == PA_F32) qv[i] = static_cast<const float*>(a.q)[src];
     else qv[i] = half_lo<DT>(static_cast<const uint16_t*>(a.q)[src]);
   }
-  // The context length is consumed here, so its load is issued before the wait for the
-  // query loads (the scheduler placed it after that wait otherwise).
-  asm volatile("" ::"s"(n_ctx));
+  PA_PIN_EARLY_SCALARS(a, n_ctx);
 #pragma unroll
   for (int i = 0; i < kQIter; ++i)
     if (tid + i * kThreads < G * D) s_q[tid + i * kThreads] = qv[i] * a.scale_log2;
@@ -1073,7 +1116,8 @@ struct Launch {
 
 template <typename K>
 void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
-  hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a);
+  hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a.ctx, a.bt, a.q,
+                        a.Pmax, a.Hkv, a.MB, a.P, a.Hq, a.split.shift, a.split.first, a);
 }
 
 template <int DT, int D, int G>
