@@ -31,9 +31,10 @@ HIPCC_FLAGS = [
 # VGPRs (the softmax rescales them with VALU instructions); in the default AGPR form the
 # compiler copied them between the register files on every K/V tile.
 # The decode kernels take their latency-critical arguments as leading scalars (see
-# PA_ATTN_LEAD_PARAMS in pa_kernels.hip); the hardware preloads those into registers.
+# PA_ATTN_LEAD_PARAMS and PA_REDUCE_LEAD_PARAMS in pa_kernels.hip); the hardware preloads
+# those into registers.
 SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
 def hipcc():

@@ -909,8 +909,33 @@ constexpr int kMaxFold = kMaxReducePartitions + kMaxPieceSlots;  // partial stat
 // large, and every extra work-group pays the fixed start-up latency.
 constexpr int kReduceWideHeads = 256;
 
+// Leading scalar arguments of reduce_kernel (preloaded into registers like those of the
+// attention kernels): the context-length address, the workspace base (= tmp_out), the
+// head counts and partition-grid size, the split packed as first << 4 | shift, and the
+// other partial arrays as offsets from the base in 256-byte units (every workspace array
+// starts on a 256-byte boundary).  The struct carries the output and the table shape.
+#define PA_REDUCE_LEAD_PARAMS                                                              \
+  const int32_t *lead_ctx, const float *lead_ws, int32_t lead_Hq, int32_t lead_Hkv,       \
+      int32_t lead_Pmax, int32_t lead_split, int32_t u_max, int32_t u_sum, int32_t u_pout, \
+      int32_t u_pmax, int32_t u_psum
+constexpr int kWsUnitFloats = 64;  // 256-byte units
+
 template <int DT, int D, int CHUNKS>
-__global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
+__global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
+                                                     const ReduceArgs args) {
+  ReduceArgs a = args;
+  a.ctx = lead_ctx;
+  a.tmp_out = lead_ws;
+  a.max_logits = lead_ws + (size_t)u_max * kWsUnitFloats;
+  a.exp_sums = lead_ws + (size_t)u_sum * kWsUnitFloats;
+  a.Hq = lead_Hq;
+  a.Hkv = lead_Hkv;
+  a.Pmax = lead_Pmax;
+  a.split.first = lead_split >> 4;
+  a.split.shift = lead_split & 15;
+  a.split.piece_out = const_cast<float*>(lead_ws) + (size_t)u_pout * kWsUnitFloats;
+  a.split.piece_max = const_cast<float*>(lead_ws) + (size_t)u_pmax * kWsUnitFloats;
+  a.split.piece_sum = const_cast<float*>(lead_ws) + (size_t)u_psum * kWsUnitFloats;
   // The weights r_q live in LDS (one per partial state); thread (pg, d4) then sums
   // r_q o_q over its partial states q = pg, pg+NPG, ... for 4 of the work-group's
   // kReduceCols columns, and the NPG partition lanes are summed in a fixed tree
@@ -953,9 +978,9 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   const float* const mls = a.max_logits;
   const float* const ess = a.exp_sums;
   const float* const tmp = a.tmp_out;
-  const long long dm = sh ? (long long)(a.split.piece_max - mls) : 0;
-  const long long ds = sh ? (long long)(a.split.piece_sum - ess) : 0;
-  const long long dO = sh ? (long long)(a.split.piece_out - tmp) : 0;
+  const long long dm = sh ? (long long)(u_pmax - u_max) * kWsUnitFloats : 0;
+  const long long ds = sh ? (long long)(u_psum - u_sum) * kWsUnitFloats : 0;
+  const long long dO = sh ? (long long)u_pout * kWsUnitFloats : 0;
   auto prow = [&](int q) { return (long long)(slot0 + q - nom_split) * G + gq; };
   auto load_o = [&](int q) {
     const long long io = q < nom_split ? (base + q) * D : dO + prow(q) * D;
@@ -983,6 +1008,9 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ReduceArgs a) {
   for (int i = 0; i < kSpecO; ++i) so[i] = load_o(min(pg + NPG * i, nom_fold - 1));
 
   int n = a.ctx[b];
+  // The output address and the table shape load within the same round trip (they are
+  // not used before it ends).
+  asm volatile("" ::"s"(n), "s"(a.out), "s"(a.MB), "s"(a.P));
   const int cap = a.MB * kBlockSize;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int nparts = (n + a.P - 1) / a.P;
@@ -1165,10 +1193,29 @@ hipError_t launch_reduce_dd(const ReduceArgs& a, int S, hipStream_t st) {
   if (fold > kMaxFold) return hipErrorInvalidValue;
   const size_t lds = (size_t)fold * sizeof(float);
   const long long heads = (long long)S * a.Hq;
+  // Workspace offsets in 256-byte units from tmp_out (see PA_REDUCE_LEAD_PARAMS).
+  const char* ws = reinterpret_cast<const char*>(a.tmp_out);
+  bool ok = true;
+  auto units = [&](const void* p) -> int32_t {
+    if (!p) return 0;
+    const long long d = reinterpret_cast<const char*>(p) - ws;
+    if (d < 0 || d % 256 || d / 256 > 0x7fffffffLL) ok = false;
+    return (int32_t)(d / 256);
+  };
+  const int32_t u_max = units(a.max_logits), u_sum = units(a.exp_sums);
+  const int32_t u_pout = units(a.split.piece_out), u_pmax = units(a.split.piece_max),
+                u_psum = units(a.split.piece_sum);
+  if (!ok || a.split.first < 0 || a.split.first >= (1 << 27) || a.split.shift > 15)
+    return hipErrorInvalidValue;
+  const int32_t split = (a.split.first << 4) | a.split.shift;
   if (heads >= kReduceWideHeads) {
-    hipLaunchKernelGGL((reduce_kernel<DT, D, 1>), dim3((unsigned)heads, 1), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((reduce_kernel<DT, D, 1>), dim3((unsigned)heads, 1), dim3(256), lds, st,
+                       a.ctx, a.tmp_out, a.Hq, a.Hkv, a.Pmax, split, u_max, u_sum, u_pout, u_pmax,
+                       u_psum, a);
   } else {
-    hipLaunchKernelGGL((reduce_kernel<DT, D, 8>), dim3((unsigned)heads, 8), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((reduce_kernel<DT, D, 8>), dim3((unsigned)heads, 8), dim3(256), lds, st,
+                       a.ctx, a.tmp_out, a.Hq, a.Hkv, a.Pmax, split, u_max, u_sum, u_pout, u_pmax,
+                       u_psum, a);
   }
   return hipGetLastError();
 }
