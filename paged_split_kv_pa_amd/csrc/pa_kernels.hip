@@ -65,6 +65,58 @@ constexpr float kRescaleSlack = 8.f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- cross-lane reductions on the vector ALU ------------------------------------------
+// __shfl_xor compiles to ds_bpermute, a round trip through the LDS crossbar per step.
+// These run on the VALU instead: lanes l ^ 1 and l ^ 2 through DPP quad permutations,
+// the lanes of a 16-lane row four and eight apart through DPP row rotations, and l ^ 16 /
+// l ^ 32 through the gfx950 half swaps (v_permlane16_swap / v_permlane32_swap: with both
+// operands x, the two results hold x of lanes l and l ^ 16, resp. l and l ^ 32).
+template <bool kSum>
+__device__ __forceinline__ float combine(float a, float b) {
+  return kSum ? a + b : fmaxf(a, b);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+template <bool kSum>
+__device__ __forceinline__ float swap_combine16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  uint32_t r0 = r[0], r1 = r[1];
+  // Without this the compiler (ROCm 7.2) combined one of the two results with itself.
+  asm("" : "+v"(r0), "+v"(r1));
+  return combine<kSum>(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+template <bool kSum>
+__device__ __forceinline__ float swap_combine32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  uint32_t r0 = r[0], r1 = r[1];
+  asm("" : "+v"(r0), "+v"(r1));
+  return combine<kSum>(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+// Sum (kSum) or max over the lanes congruent to this lane modulo kFrom (a power of two
+// <= 32): every lane of such a group ends up with the group's result (bitwise the same
+// in all of them for the max; for the sum, the result a given lane reads is the same
+// from run to run).
+template <bool kSum, int kFrom>
+__device__ __forceinline__ float lane_reduce(float x) {
+  static_assert(kFrom >= 1 && kFrom <= 32 && (kFrom & (kFrom - 1)) == 0, "power of two");
+  if constexpr (kFrom <= 1) x = combine<kSum>(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  if constexpr (kFrom <= 2) x = combine<kSum>(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  if constexpr (kFrom <= 4) x = combine<kSum>(x, dpp_mov<0x124>(x));  // row_ror:4
+  if constexpr (kFrom <= 8) x = combine<kSum>(x, dpp_mov<0x128>(x));  // row_ror:8
+  if constexpr (kFrom <= 16) x = swap_combine16<kSum>(x);
+  return swap_combine32<kSum>(x);
+}
+// Sum over the four lanes of a quad (l ^ 1, l ^ 2), bitwise the same in all four.
+__device__ __forceinline__ float lane_reduce_quad(float x) {
+  x += dpp_mov<0xB1>(x);
+  return x + dpp_mov<0x4E>(x);
+}
+
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 raw-buffer format word).
 // A load at an offset >= bytes returns zeros without touching memory, so a
 // resource with bytes = 0 turns every load through it into a no-op.
@@ -448,8 +500,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (4 * kg + i < valid) ? s[i] * a.scale_log2 : kNegInf;
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = lane_reduce<false, 16>(bm);
     m_max = fmaxf(m_max, bm);
     if (__any(bm > m_ref + kRescaleSlack)) {
       const float m_new = fmaxf(m_ref, bm);
@@ -533,8 +584,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   }
 
   // ---- merge the NW waves' states (log-sum-exp) ----
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = lane_reduce<true, 16>(l_run);
   if (kg == 0) {
     s_mref[w][r16] = m_ref;
     s_mmax[w][r16] = m_max;
@@ -760,14 +810,10 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float sv = acc[h];
-      sv += __shfl_xor(sv, 1);
-      sv += __shfl_xor(sv, 2);
+      sv = lane_reduce_quad(sv);
       x[h] = t < valid ? sv : kNegInf;
       float v = x[h];
-      v = fmaxf(v, __shfl_xor(v, 4));
-      v = fmaxf(v, __shfl_xor(v, 8));
-      v = fmaxf(v, __shfl_xor(v, 16));
-      v = fmaxf(v, __shfl_xor(v, 32));
+      v = lane_reduce<false, 4>(v);
       bm[h] = v;
       m_max[h] = fmaxf(m_max[h], v);
       move |= v > m_ref[h] + kRescaleSlack;
@@ -834,8 +880,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float l = l_run[h];
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) l += __shfl_xor(l, s);
+    l = lane_reduce<true, 1>(l);
     l_run[h] = l;
   }
   __syncthreads();  // every wave is done with s_q / s_p; their bytes become s_o
@@ -1043,8 +1088,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
     load_ms(q, m, s);
     put_max(q, m);
   }
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+  mx = lane_reduce<false, 1>(mx);
   if (lane == 0) s_red[wv] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
@@ -1067,8 +1111,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
     s_w[q] = r;
     wsum += r;
   }
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) wsum += __shfl_xor(wsum, x);
+  wsum = lane_reduce<true, 1>(wsum);
   __syncthreads();  // weights visible; s_red reads of M done
   if (lane == 0) s_red[wv] = wsum;
 
@@ -1080,12 +1123,12 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
 #pragma unroll 4
   for (int q = pg + NPG * kSpecO; q < nfold; q += NPG) acc += load_o(q) * s_w[q];
 
-  // Lanes NC4 apart in a wave hold the same columns: shuffle steps sum a wave's
+  // Lanes NC4 apart in a wave hold the same columns: cross-lane steps sum a wave's
   // partition lanes, then the 4 waves meet in LDS.
+  if constexpr (NC4 < 64) {
 #pragma unroll
-  for (int x = NC4; x < 64; x <<= 1)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], x);
+    for (int j = 0; j < 4; ++j) acc[j] = lane_reduce<true, NC4>(acc[j]);
+  }
   if (lane < NC4) s_acc[wv][d4] = acc;
   __syncthreads();
   if (tid < NC4) {
