@@ -34,7 +34,7 @@ HIPCC_FLAGS = [
 # PA_ATTN_LEAD_PARAMS and PA_REDUCE_LEAD_PARAMS in pa_kernels.hip); the hardware preloads
 # those into registers.
 SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
+                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"]}
 
 
 def hipcc():

@@ -216,12 +216,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 #define PA_ATTN_LEAD_PARAMS                                                                \
   const int32_t *lead_ctx, const int32_t *lead_bt, const void *lead_q, int32_t lead_Pmax, \
       int32_t lead_Hkv, int32_t lead_MB, int32_t lead_P, int32_t lead_Hq,                 \
-      int32_t lead_shift, int32_t lead_first
+      int32_t lead_shift, int32_t lead_first, int32_t lead_order
 
 __device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, const int32_t* bt,
                                               const void* q, int32_t Pmax, int32_t Hkv,
                                               int32_t MB, int32_t P, int32_t Hq, int32_t shift,
-                                              int32_t first) {
+                                              int32_t first, int32_t order) {
   a.ctx = ctx;
   a.bt = bt;
   a.q = q;
@@ -232,11 +232,12 @@ __device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, co
   a.Hq = Hq;
   a.split.shift = shift;
   a.split.first = first;
+  a.order_seqs = order;
   return a;
 }
 #define PA_ATTN_APPLY_LEAD(args)                                                        \
   with_lead(args, lead_ctx, lead_bt, lead_q, lead_Pmax, lead_Hkv, lead_MB, lead_P, lead_Hq, \
-            lead_shift, lead_first)
+            lead_shift, lead_first, lead_order)
 
 // Consumes the context length and one field of each 64-byte line of the argument
 // struct (output, K/V bases, pool size and scale), so that their scalar loads are issued
@@ -311,6 +312,34 @@ __device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it
   return r;
 }
 
+// Longest-first order for V1 (one work-group per (sequence, KV head), the whole context):
+// work-groups are dispatched in grid order, so with more of them than fit on the chip at
+// once, a long sequence dispatched late runs on after the others have finished; taking
+// sequences longest context first shortens that tail (batched 256 x U{512..4096}: a
+// fluid model of the dispatch gives ~229 us in grid order and ~206 us longest first).
+// The work-group of rank r (blockIdx.z) takes the sequence with exactly r sequences
+// before it in the order (longer context, or equal and lower index): every work-group
+// reads all S context lengths (one coalesced round trip) and counts.  The rank of each
+// sequence is distinct, so exactly one thread writes the pick.  The result of each
+// (sequence, head) does not depend on which work-group computes it.
+__device__ __forceinline__ int seq_of_length_rank(const int32_t* ctx, int S, int r, int* s_len,
+                                                  int* s_pick) {
+  for (int t = threadIdx.x; t < S; t += blockDim.x) s_len[t] = ctx[t];
+  __syncthreads();
+  for (int c = threadIdx.x; c < S; c += blockDim.x) {
+    const int lc = s_len[c];
+    int rank = 0;
+#pragma unroll 8
+    for (int k = 0; k < S; ++k) {
+      const int lk = s_len[k];
+      rank += (lk > lc) | ((lk == lc) & (k < c));
+    }
+    if (rank == r) *s_pick = c;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
 // Rows of the partial state of query head h of this work-group's group: the
 // partition's row of tmp_out / max_logits / exp_sums, or the piece's slot.
 template <int G, int D>
@@ -379,8 +408,11 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   unsigned char s_un[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
   typedef float MergeRows[NMM * 4][64];
   MergeRows* s_o = reinterpret_cast<MergeRows*>(s_un);
+  __shared__ int s_len[kOrderMaxSeqs];
+  __shared__ int s_pick;
 
-  const Item it = grid_item(a);
+  Item it = grid_item(a);
+  if (a.order_seqs > 0) it.b = seq_of_length_rank(a.ctx, a.order_seqs, it.b, s_len, &s_pick);
   const int g = it.g, b = it.b;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
@@ -1154,6 +1186,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
 //       and drains too often: mixed_d256 at partition 256, 72.6 vs 69.2 us), else 0
 //       (more waves for small grids).
 constexpr int kAutoVariant = -1;
+constexpr long long kOrderMinItems = 256;  // longest-first V1 order from this many items
 constexpr long long kAutoOneWaveGrid = 512;
 constexpr int kAutoFourWaveBlocks = 64;
 constexpr int kAutoOneWaveMinBlocksD256 = 32;
@@ -1188,7 +1221,8 @@ struct Launch {
 template <typename K>
 void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
   hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a.ctx, a.bt, a.q,
-                        a.Pmax, a.Hkv, a.MB, a.P, a.Hq, a.split.shift, a.split.first, a);
+                        a.Pmax, a.Hkv, a.MB, a.P, a.Hq, a.split.shift, a.split.first,
+                        a.order_seqs, a);
 }
 
 template <int DT, int D, int G>
@@ -1295,10 +1329,17 @@ hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& 
     grid = dim3((unsigned)wgs, 1, 1);
   }
   const Launch l{grid, stream, ev_start, ev_stop};
+  // Longest-first order for V1 on the matrix-core kernel when the grid has more (sequence,
+  // KV head) items than compute units, i.e. runs in more than one wave of work-groups.
+  AttnArgs ao = a;
+  ao.order_seqs = 0;
+  if (a.Pmax == 1 && a.split.shift == 0 && kernel_for(dtype, group) == Kernel::kMfma &&
+      num_seqs <= kOrderMaxSeqs && (long long)num_seqs * a.Hkv >= kOrderMinItems)
+    ao.order_seqs = num_seqs;
   switch (dtype) {
-    case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, a, l);
-    case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, a, l);
-    case PA_BF16: return launch_attn_d<PA_BF16>(head_dim, group, a, l);
+    case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, ao, l);
+    case PA_F16: return launch_attn_d<PA_F16>(head_dim, group, ao, l);
+    case PA_BF16: return launch_attn_d<PA_BF16>(head_dim, group, ao, l);
     default: return hipErrorInvalidValue;
   }
 }
