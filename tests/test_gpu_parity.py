@@ -246,6 +246,41 @@ def test_table_entries_past_the_context_are_never_dereferenced(dtype, G, D):
     assert torch.equal(got, clean)
 
 
+@pytest.mark.parametrize("S,dtype,G", [(300, "bf16", 8), (512, "f16", 4), (513, "bf16", 8)])
+def test_v1_many_sequences_in_longest_first_order(S, dtype, G):
+    """V1 over many sequences (from 256 (sequence, KV head) items up to 512 sequences the
+    work-groups take sequences longest context first; 513 is past that limit): parity
+    with the oracle, ties and empty sequences included, and every sequence's rows
+    bitwise equal to a decode of that sequence alone with the same kernel shape."""
+    rng = np.random.default_rng(S)
+    ctx = rng.integers(1, 700, size=S)
+    ctx[::7] = 333   # ties
+    ctx[3::11] = 0   # empty sequences
+    ctx[5] = 1
+    w = small_workload(40 + S, ctx.tolist(), Hq=2 * G, Hkv=2, D=128, dtype=dtype)
+    dev = upload(w)
+    ref = oracle.decode_attention(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                                  w.scale, w.dtype)
+    old = B.pa_get_mfma_variant()
+    try:
+        say(f"v1 order S={S} dtype={dtype} G={G}")
+        out = run_path(w, dev, B.PA_PATH_V1, 512, variant=2)
+        check_close(to_f64(out), ref, f"v1 order S={S}")
+        assert torch.all(out[ctx == 0] == 0)
+        for b in [0, 3, 5, 7, int(np.argmax(ctx)), int(np.argmin(ctx)), S // 2, S - 1]:
+            say(f"v1 order S={S}: sequence {b} alone")
+            q1 = dev["q"][b:b + 1].clone()  # fresh (16-byte aligned) single-sequence inputs
+            one = torch.empty_like(q1)
+            B.pa_decode_ex(one, q1, dev["k_cache"], dev["v_cache"],
+                           dev["block_tables"][b:b + 1].clone(),
+                           dev["context_lens"][b:b + 1].clone(), w.scale, 512,
+                           path=B.PA_PATH_V1)
+            torch.cuda.synchronize()
+            assert torch.equal(one[0], out[b]), f"sequence {b}"
+    finally:
+        B.pa_set_mfma_variant(old)
+
+
 def test_identity_coded_values_select_exact_rows():
     """fp32 V = physical_block*16 + slot, q = 0: out is the mean of the selected codes."""
     ctx = [1000, 333, 16, 1]
