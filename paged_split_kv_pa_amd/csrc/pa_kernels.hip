@@ -1175,21 +1175,20 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
 // ---- dispatch --------------------------------------------------------------------------
 // Work-group shape of the matrix-core kernel (see attn_mfma_kernel):
 //   0 = 2 waves, pipeline depth 3 (head_dim 128) / 2 (head_dim 256)
-//   1 = 1 wave,  pipeline depth 5 / 3
+//   1 = 1 wave,  pipeline depth 2 (one block in flight while the previous one is used)
 //   2 = 4 waves, pipeline depth 2
 //  -1 = automatic (default): 2 when a work-group streams more than 64 blocks (a
 //       partition longer than 1024 tokens, i.e. V1 over long contexts: four waves
-//       share its blocks; batched 256 x U{512..4096}: 227 vs 236 us), else 1 when the
-//       grid has at least two work-groups per compute unit (the long-context V2 shape
-//       streams best with one wave per work-group) and, at head_dim 256, a partition
-//       spans at least 32 blocks (with 16 blocks, the one-wave pipeline of depth 3 fills
-//       and drains too often: mixed_d256 at partition 256, 72.6 vs 69.2 us), else 0
-//       (more waves for small grids).
+//       share its blocks; batched 256 x U{512..4096}: 199 us, 224 with two waves), else
+//       1 when the grid has at least two work-groups per compute unit (long_100k 38.9
+//       us/step, against 40.2 with the same wave 5 deep and 39.4 3 deep; mixed_d256 at
+//       partition 512 and 256 likewise), else 0 (more waves for small grids: single_8k
+//       11.5 us, 11.9 with one wave).  More loads in flight per compute unit measured
+//       slower, not faster, on every shape tried.
 constexpr int kAutoVariant = -1;
 constexpr long long kOrderMinItems = 256;  // longest-first V1 order from this many items
 constexpr long long kAutoOneWaveGrid = 512;
 constexpr int kAutoFourWaveBlocks = 64;
-constexpr int kAutoOneWaveMinBlocksD256 = 32;
 std::atomic<int> g_mfma_variant{-2};  // -2: not yet read from the environment
 
 int mfma_variant_setting() {
@@ -1203,11 +1202,10 @@ int mfma_variant_setting() {
   return v;
 }
 
-int mfma_variant(const dim3& grid, int partition_tokens, int head_dim) {
+int mfma_variant(const dim3& grid, int partition_tokens) {
   const int v = mfma_variant_setting();
   if (v != kAutoVariant) return v;
   if (partition_tokens > kAutoFourWaveBlocks * kBlockSize) return 2;
-  if (head_dim == 256 && partition_tokens < kAutoOneWaveMinBlocksD256 * kBlockSize) return 0;
   const long long wgs = (long long)grid.x * grid.y * grid.z;
   return wgs >= kAutoOneWaveGrid ? 1 : 0;
 }
@@ -1228,9 +1226,9 @@ void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
 template <int DT, int D, int G>
 hipError_t launch_attn_t(const AttnArgs& a, const Launch& l) {
   if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
-    switch (mfma_variant(l.grid, a.P, D)) {
+    switch (mfma_variant(l.grid, a.P)) {
       case 0: launch(attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>, l, 2 * 64, a); break;
-      case 1: launch(attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>, l, 64, a); break;
+      case 1: launch(attn_mfma_kernel<DT, D, G, 1, 2>, l, 64, a); break;
       default: launch(attn_mfma_kernel<DT, D, G, 4, 2>, l, 4 * 64, a); break;
     }
   } else {
