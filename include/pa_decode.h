@@ -238,8 +238,10 @@ const char* pa_version(void);
  *       (D=256) register pipeline per wave
  *   1 = 1 wave, 2-deep pipeline
  *   2 = 4 waves, 2-deep pipeline
+ *   3 = 1 wave, 5-deep / 3-deep pipeline
  *  -1 = automatic (the default): 2 when a work-group covers more than 1024
- *       tokens, else 1 for grids of >= 512 work-groups, else 0.
+ *       tokens, else for grids of >= 512 work-groups 1 (V2) or 3 (V1),
+ *       else 0.
  * All variants compute the same result (to rounding).  The environment
  * variable PA_MFMA_VARIANT sets the initial value.  Process-wide; do not
  * change it while another thread is launching.  Returns PA_ERR_UNSUPPORTED

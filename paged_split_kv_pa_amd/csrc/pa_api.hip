@@ -640,7 +640,7 @@ const char* pa_version(void) { return "pa_decode 0.1.0 gfx950"; }
 
 pa_status_t pa_set_mfma_variant(int32_t variant) {
   if (pa::set_mfma_variant(variant) != 0)
-    return fail(PA_ERR_UNSUPPORTED, "matrix-core variant %d unknown (-1, 0, 1 or 2)", variant);
+    return fail(PA_ERR_UNSUPPORTED, "matrix-core variant %d unknown (-1, 0, 1, 2 or 3)", variant);
   return ok();
 }
 

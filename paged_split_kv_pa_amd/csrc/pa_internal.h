@@ -47,9 +47,9 @@ struct AttnArgs {
   int32_t P;                 // tokens per partition (multiple of 16)
   int32_t Pmax;              // partition-grid size
   Split split;
-  // > 0 (only with Pmax == 1 and no split, on the matrix-core kernel): the number of
-  // sequences S; work-group z then takes the sequence of rank z in longest-context-first
-  // order instead of sequence z (see attn_mfma_kernel).
+  // > 0 (only with Pmax == 1 and no split, on the four-wave matrix-core kernel): the
+  // number of sequences S; work-group z then takes the sequence of rank z in
+  // longest-context-first order instead of sequence z (see attn_mfma_kernel).
   int32_t order_seqs = 0;
 };
 constexpr int kOrderMaxSeqs = 512;  // longest-first V1 order: at most this many sequences

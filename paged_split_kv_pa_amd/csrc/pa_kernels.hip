@@ -324,15 +324,21 @@ __device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it
 // (sequence, head) does not depend on which work-group computes it.
 __device__ __forceinline__ int seq_of_length_rank(const int32_t* ctx, int S, int r, int* s_len,
                                                   int* s_pick) {
-  for (int t = threadIdx.x; t < S; t += blockDim.x) s_len[t] = ctx[t];
+  for (int t = threadIdx.x; t < ((S + 3) & ~3); t += blockDim.x)
+    s_len[t] = t < S ? ctx[t] : INT32_MIN;
   __syncthreads();
+  // Lengths are compared four at a time (16-byte LDS reads, the same address in every
+  // lane); the padding entries (INT32_MIN, index >= S) are never ordered first.
   for (int c = threadIdx.x; c < S; c += blockDim.x) {
     const int lc = s_len[c];
     int rank = 0;
-#pragma unroll 8
-    for (int k = 0; k < S; ++k) {
-      const int lk = s_len[k];
-      rank += (lk > lc) | ((lk == lc) & (k < c));
+#pragma unroll 4
+    for (int k = 0; k < S; k += 4) {
+      const int4 l4 = *reinterpret_cast<const int4*>(s_len + k);
+      rank += (l4.x > lc) | ((l4.x == lc) & (k < c));
+      rank += (l4.y > lc) | ((l4.y == lc) & (k + 1 < c));
+      rank += (l4.z > lc) | ((l4.z == lc) & (k + 2 < c));
+      rank += (l4.w > lc) | ((l4.w == lc) & (k + 3 < c));
     }
     if (rank == r) *s_pick = c;
   }
@@ -408,11 +414,15 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   unsigned char s_un[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
   typedef float MergeRows[NMM * 4][64];
   MergeRows* s_o = reinterpret_cast<MergeRows*>(s_un);
-  __shared__ int s_len[kOrderMaxSeqs];
+  // Longest-first order (see seq_of_length_rank): built into the four-wave shape only,
+  // the one used for partitions long enough for the ordering to pay.
+  __shared__ __attribute__((aligned(16))) int s_len[NW == 4 ? kOrderMaxSeqs : 4];
   __shared__ int s_pick;
 
   Item it = grid_item(a);
-  if (a.order_seqs > 0) it.b = seq_of_length_rank(a.ctx, a.order_seqs, it.b, s_len, &s_pick);
+  if constexpr (NW == 4) {
+    if (a.order_seqs > 0) it.b = seq_of_length_rank(a.ctx, a.order_seqs, it.b, s_len, &s_pick);
+  }
   const int g = it.g, b = it.b;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
@@ -1177,14 +1187,16 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
 //   0 = 2 waves, pipeline depth 3 (head_dim 128) / 2 (head_dim 256)
 //   1 = 1 wave,  pipeline depth 2 (one block in flight while the previous one is used)
 //   2 = 4 waves, pipeline depth 2
+//   3 = 1 wave,  pipeline depth 5 / 3
 //  -1 = automatic (default): 2 when a work-group streams more than 64 blocks (a
 //       partition longer than 1024 tokens, i.e. V1 over long contexts: four waves
-//       share its blocks; batched 256 x U{512..4096}: 199 us, 224 with two waves), else
-//       1 when the grid has at least two work-groups per compute unit (long_100k 38.9
-//       us/step, against 40.2 with the same wave 5 deep and 39.4 3 deep; mixed_d256 at
-//       partition 512 and 256 likewise), else 0 (more waves for small grids: single_8k
-//       11.5 us, 11.9 with one wave).  More loads in flight per compute unit measured
-//       slower, not faster, on every shape tried.
+//       share its blocks; batched 256 x U{512..4096}: 199 us, 224 with two waves); else,
+//       for grids of at least two work-groups per compute unit, 1 in phase 1 of V2
+//       (cold KV: long_100k 38.9 us/step against 40.2 with the same wave 5 deep and 39.4
+//       3 deep, mixed_d256 at partition 512 and 256 likewise; more loads in flight per
+//       compute unit measured slower) and 3 in V1 (many short sequences: with cache-warm
+//       KV, 256 x 256 tokens took 23 us 5 deep and 48 us 2 deep); else 0 (more waves for
+//       small grids: single_8k 11.5 us, 11.9 with one wave).
 constexpr int kAutoVariant = -1;
 constexpr long long kOrderMinItems = 256;  // longest-first V1 order from this many items
 constexpr long long kAutoOneWaveGrid = 512;
@@ -1196,18 +1208,19 @@ int mfma_variant_setting() {
   if (v == -2) {
     v = kAutoVariant;
     const char* e = std::getenv("PA_MFMA_VARIANT");
-    if (e && (e[0] == '0' || e[0] == '1' || e[0] == '2') && e[1] == '\0') v = e[0] - '0';
+    if (e && e[0] >= '0' && e[0] <= '3' && e[1] == '\0') v = e[0] - '0';
     g_mfma_variant.store(v, std::memory_order_relaxed);
   }
   return v;
 }
 
-int mfma_variant(const dim3& grid, int partition_tokens) {
+int mfma_variant(const dim3& grid, int partition_tokens, bool single_pass) {
   const int v = mfma_variant_setting();
   if (v != kAutoVariant) return v;
   if (partition_tokens > kAutoFourWaveBlocks * kBlockSize) return 2;
   const long long wgs = (long long)grid.x * grid.y * grid.z;
-  return wgs >= kAutoOneWaveGrid ? 1 : 0;
+  if (wgs < kAutoOneWaveGrid) return 0;
+  return single_pass ? 3 : 1;
 }
 
 struct Launch {
@@ -1226,9 +1239,10 @@ void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
 template <int DT, int D, int G>
 hipError_t launch_attn_t(const AttnArgs& a, const Launch& l) {
   if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
-    switch (mfma_variant(l.grid, a.P)) {
+    switch (mfma_variant(l.grid, a.P, a.Pmax == 1)) {
       case 0: launch(attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>, l, 2 * 64, a); break;
       case 1: launch(attn_mfma_kernel<DT, D, G, 1, 2>, l, 64, a); break;
+      case 3: launch(attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>, l, 64, a); break;
       default: launch(attn_mfma_kernel<DT, D, G, 4, 2>, l, 4 * 64, a); break;
     }
   } else {
@@ -1305,7 +1319,7 @@ hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
 }  // namespace
 
 int set_mfma_variant(int v) {
-  if (v < kAutoVariant || v > 2) return -1;
+  if (v < kAutoVariant || v > 3) return -1;
   g_mfma_variant.store(v, std::memory_order_relaxed);
   return 0;
 }
@@ -1328,11 +1342,17 @@ hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& 
   }
   const Launch l{grid, stream, ev_start, ev_stop};
   // Longest-first order for V1 on the matrix-core kernel when the grid has more (sequence,
-  // KV head) items than compute units, i.e. runs in more than one wave of work-groups.
+  // KV head) items than compute units, i.e. runs in more than one wave of work-groups,
+  // and a work-group covers more than 1024 tokens (the four-wave shape).  The ordering
+  // costs each work-group a few microseconds (the ranking and one more dependent round
+  // trip): with 256 sequences of 256 tokens that doubled the step (23 -> 49 us), with
+  // 2048 tokens it costs ~7 us when all lengths are equal, and with U{512..4096} lengths
+  // it saves ~27 us.
   AttnArgs ao = a;
   ao.order_seqs = 0;
   if (a.Pmax == 1 && a.split.shift == 0 && kernel_for(dtype, group) == Kernel::kMfma &&
-      num_seqs <= kOrderMaxSeqs && (long long)num_seqs * a.Hkv >= kOrderMinItems)
+      num_seqs <= kOrderMaxSeqs && (long long)num_seqs * a.Hkv >= kOrderMinItems &&
+      a.P > kAutoFourWaveBlocks * kBlockSize)
     ao.order_seqs = num_seqs;
   switch (dtype) {
     case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, ao, l);

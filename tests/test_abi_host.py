@@ -229,10 +229,10 @@ def test_path_rules():
 def test_mfma_variant_knob():
     old = B.pa_get_mfma_variant()
     try:
-        for v in (0, 1, 2, -1):
+        for v in (0, 1, 2, 3, -1):
             B.pa_set_mfma_variant(v)
             assert B.pa_get_mfma_variant() == v
-        for bad in (3, -2):
+        for bad in (4, -2):
             with pytest.raises(B.PaError):
                 B.pa_set_mfma_variant(bad)
     finally:

@@ -81,7 +81,7 @@ def test_config_parity(cfg, P, path):
     check_close(to_f64(out), ref, f"{wl.CONFIG_NAMES[cfg]} P={P} path={path}")
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, -1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, -1])
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_mfma_variants(cfg, variant):
     w, dev, ref = config_case(cfg)
@@ -248,12 +248,14 @@ def test_table_entries_past_the_context_are_never_dereferenced(dtype, G, D):
 
 @pytest.mark.parametrize("S,dtype,G", [(300, "bf16", 8), (512, "f16", 4), (513, "bf16", 8)])
 def test_v1_many_sequences_in_longest_first_order(S, dtype, G):
-    """V1 over many sequences (from 256 (sequence, KV head) items up to 512 sequences the
-    work-groups take sequences longest context first; 513 is past that limit): parity
-    with the oracle, ties and empty sequences included, and every sequence's rows
-    bitwise equal to a decode of that sequence alone with the same kernel shape."""
+    """V1 over many sequences (from 256 (sequence, KV head) items up to 512 sequences,
+    with contexts bounded above 1024 tokens, the work-groups take sequences longest
+    context first; 513 is past that limit): parity with the oracle, ties and empty
+    sequences included, and every sequence's rows bitwise equal to a decode of that
+    sequence alone with the same kernel shape."""
     rng = np.random.default_rng(S)
-    ctx = rng.integers(1, 700, size=S)
+    ctx = rng.integers(1, 1400, size=S)
+    ctx[1] = 1399    # table bound > 1024 tokens
     ctx[::7] = 333   # ties
     ctx[3::11] = 0   # empty sequences
     ctx[5] = 1
