@@ -52,7 +52,7 @@ struct AttnArgs {
   // longest-context-first order instead of sequence z (see attn_mfma_kernel).
   int32_t order_seqs = 0;
 };
-constexpr int kOrderMaxSeqs = 512;  // longest-first V1 order: at most this many sequences
+constexpr int kOrderMaxSeqs = 512;  // longest-first orders (V1, prefill): at most this many sequences
 
 // Arguments of the phase-2 (cross-partition) kernel.
 struct ReduceArgs {
@@ -113,6 +113,9 @@ struct PrefillArgs {
   const int32_t* query_start;  // [S + 1]
   float scale_log2;          // scale * log2(e)
   int32_t T, Hq, Hkv, NB, MB;
+  // > 0: the number of sequences S; work-group z then takes the sequence of rank z in
+  // most-keys-first order (prefix plus new tokens), and position blocks run last first.
+  int32_t order_seqs = 0;
 };
 // Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128 or 256,
 // fp16/bf16.  e0 / e1 (may be null) are recorded when the kernel starts / ends.

@@ -130,7 +130,36 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
 // of 16 rows per K operand, and the 8-byte transposing reads of 8 rows per half-wave for
 // V; a 256-byte row conflicts 28 cycles per K read, a 272-byte row 4).
 
-template <int DT, int G, int D>
+// Most-keys-first order over sequences.  A work-group's work grows with the keys it
+// attends to (its sequence's prefix plus the new tokens up to its positions), and
+// work-groups start in grid order: a sequence with a long prefix whose work-groups start
+// last runs on alone at the end (4 sequences with 4096 / 0 / 1000 / 16384-token prefixes:
+// the 16384 one came last).  Work-group z takes the sequence with exactly z sequences
+// before it (more keys, or as many and a lower index), from every sequence's prefix plus
+// new-token count (one round trip for all of them), and its position blocks run last
+// first (the last ones attend to the most keys).  The result of each (sequence, head,
+// position) does not depend on which work-group computes it.
+__device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int r,
+                                               long long* s_key, int* s_pick) {
+  for (int t = threadIdx.x; t < S; t += blockDim.x)
+    s_key[t] = (long long)a.ctx[t] + ((long long)a.query_start[t + 1] - a.query_start[t]);
+  __syncthreads();
+  for (int c = threadIdx.x; c < S; c += blockDim.x) {
+    const long long kc = s_key[c];
+    int rank = 0;
+    for (int k = 0; k < S; ++k) {
+      const long long kk = s_key[k];
+      rank += (kk > kc) | ((kk == kc) & (k < c));
+    }
+    if (rank == r) *s_pick = c;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
+// kOrder: the most-keys-first order above (launches with several sequences); a separate
+// instantiation, so the one-sequence kernel's register allocation is untouched.
+template <int DT, int G, int D, bool kOrder>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
   using Sh = Shape<D>;
@@ -138,9 +167,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   constexpr int kPos = Sh::ROWS / G;  // query positions per work-group
   __shared__ u32x4 s_k[2][kTile * ROW];
   __shared__ u32x4 s_v[2][kTile * ROW];
+  __shared__ int s_pick;
 
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int p0 = blockIdx.x * kPos;
+  const int g = blockIdx.y;
+  int b = blockIdx.z, xb = blockIdx.x;
+  if constexpr (kOrder) {
+    // The key counts live in the first K tile buffer, which is not written before the
+    // barrier that ends the ranking.
+    b = seq_of_key_rank(a, a.order_seqs, b, reinterpret_cast<long long*>(s_k[0]), &s_pick);
+    xb = gridDim.x - 1 - blockIdx.x;
+  }
+  const int p0 = xb * kPos;
   int r1 = a.query_start[b + 1], r0 = a.query_start[b];
   r1 = min(r1, a.T);
   r0 = min(max(r0, 0), r1);
@@ -466,21 +503,30 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 }
 
+template <int DT, int D, bool kOrder>
+hipError_t launch_gg(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
+                     hipEvent_t e1) {
+  const dim3 block(kThreads);
+  switch (G) {
+    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_g(int G, const PrefillArgs& a, int num_seqs, int max_query_len,
                     hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const int per = Shape<D>::ROWS / G;
   const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
-  const dim3 block(kThreads);
-  switch (G) {
-    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D>), grid, block, 0, st, e0, e1, 0, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  PrefillArgs ao = a;
+  ao.order_seqs = num_seqs >= 2 && num_seqs <= kOrderMaxSeqs ? num_seqs : 0;
+  if (ao.order_seqs > 0) return launch_gg<DT, D, true>(G, grid, ao, st, e0, e1);
+  return launch_gg<DT, D, false>(G, grid, ao, st, e0, e1);
 }
 
 }  // namespace

@@ -86,6 +86,26 @@ def test_pf_batch_mixed():
     check_rows(to_f64(run(w, upload(w))), reference(w), "pf_batch_mixed")
 
 
+def test_pf_batch_mixed_rows_equal_single_sequence_runs():
+    """With several sequences the work-groups take sequences most keys first (the longest
+    prefix plus chunk first) and position blocks last first; every sequence's rows must be
+    bitwise those of a prefill of that sequence alone (one sequence: grid order)."""
+    w = wl.prefill_config(2)
+    dev = upload(w)
+    batch = run(w, dev)
+    qs = np.asarray(w.query_start)
+    for b in range(len(w.context_lens)):
+        r0, r1 = int(qs[b]), int(qs[b + 1])
+        say(f"prefill {w.name}: sequence {b} alone (rows {r0}..{r1})")
+        one = {n: dev[n][r0:r1].clone() for n in ("q", "k_new", "v_new")}
+        one["k_cache"], one["v_cache"] = dev["k_cache"], dev["v_cache"]
+        one["block_tables"] = dev["block_tables"][b:b + 1].clone()
+        one["context_lens"] = dev["context_lens"][b:b + 1].clone()
+        one["query_start"] = torch.tensor([0, r1 - r0], dtype=torch.int32, device="cuda")
+        got = run(w, one)
+        assert torch.equal(got, batch[r0:r1]), f"sequence {b}"
+
+
 def test_pf_chunk_sampled_rows():
     """The 8192-token chunk after a 65536-token prefix: 96 sampled (row, head) outputs
     against the oracle's causal rows, one at a time."""
