@@ -312,6 +312,68 @@ __device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it
   return r;
 }
 
+// Compacted order for V2 with several sequences (no work split): the grid has Pmax
+// partition slots per (sequence, KV head), and the slots past a sequence's context are
+// empty.  Work-groups are placed on compute units in grid order, so with sequences of
+// very different lengths the real items of the long ones pile up on the same units
+// (mixed 65536..1-token contexts: up to 6 partitions on one unit, 1.9 on average;
+// 256 x U{512..4096}: 32 against 18).  Work-group j (linear grid index) instead takes
+// the j-th real item in (sequence, KV head, partition) order, so real items are
+// contiguous in dispatch order; work-groups past the last one return.  A sequence with
+// no tokens still has one item (partition 0), whose work-group writes its zero output.
+// Each wave derives its item from all S context lengths: lane l sums the partition
+// counts of sequences 8l .. 8l+7 (S <= 512), a wave scan gives each lane's first item,
+// and the lane whose range holds j finds the sequence.
+__device__ __forceinline__ bool compact_item(const AttnArgs& a, int S, Item& it) {
+  const int j = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int lane = threadIdx.x & 63;
+  const int cap = a.MB * kBlockSize;
+  int np[8];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 8 * lane + i;
+    int n = t < S ? a.ctx[t] : 0;
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    int c = (n + a.P - 1) / a.P;
+    c = c > a.Pmax ? a.Pmax : (c < 1 ? 1 : c);
+    np[i] = t < S ? c : 0;
+    tot += np[i];
+  }
+  int incl = tot;  // inclusive scan of the lane totals
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int first = (incl - tot) * a.Hkv;  // items are (sequence, KV head, partition)
+  const unsigned long long hit = __ballot(j >= first && j < incl * a.Hkv);
+  if (hit == 0) return false;
+  const int owner = __builtin_ctzll(hit);
+  int seq = 0, off = 0, cnt = 1;
+  if (lane == owner) {
+    int rem = j - first;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int items = np[i] * a.Hkv;
+      if (rem >= 0 && rem < items) {
+        seq = 8 * lane + i;
+        off = rem;
+        cnt = np[i];
+      }
+      rem -= items;
+    }
+  }
+  seq = __builtin_amdgcn_readlane(seq, owner);
+  off = __builtin_amdgcn_readlane(off, owner);
+  cnt = __builtin_amdgcn_readlane(cnt, owner);
+  it.b = seq;
+  it.g = off / cnt;
+  it.p = off - it.g * cnt;
+  it.piece = -1;
+  return true;
+}
+
 // Longest-first order for V1 (one work-group per (sequence, KV head), the whole context):
 // work-groups are dispatched in grid order, so with more of them than fit on the chip at
 // once, a long sequence dispatched late runs on after the others have finished; taking
@@ -420,8 +482,12 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   __shared__ int s_pick;
 
   Item it = grid_item(a);
-  if constexpr (NW == 4) {
-    if (a.order_seqs > 0) it.b = seq_of_length_rank(a.ctx, a.order_seqs, it.b, s_len, &s_pick);
+  if (a.order_seqs > 0) {
+    if (a.Pmax > 1) {
+      if (!compact_item(a, a.order_seqs, it)) return;  // past the last item
+    } else if constexpr (NW == 4) {
+      it.b = seq_of_length_rank(a.ctx, a.order_seqs, it.b, s_len, &s_pick);
+    }
   }
   const int g = it.g, b = it.b;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -1348,11 +1414,14 @@ hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& 
   // trip): with 256 sequences of 256 tokens that doubled the step (23 -> 49 us), with
   // 2048 tokens it costs ~7 us when all lengths are equal, and with U{512..4096} lengths
   // it saves ~27 us.
+  // With V2 (Pmax > 1), several sequences and no split: the compacted item order.
   AttnArgs ao = a;
   ao.order_seqs = 0;
-  if (a.Pmax == 1 && a.split.shift == 0 && kernel_for(dtype, group) == Kernel::kMfma &&
-      num_seqs <= kOrderMaxSeqs && (long long)num_seqs * a.Hkv >= kOrderMinItems &&
-      a.P > kAutoFourWaveBlocks * kBlockSize)
+  const bool mfma = kernel_for(dtype, group) == Kernel::kMfma;
+  if (a.Pmax == 1 && a.split.shift == 0 && mfma && num_seqs <= kOrderMaxSeqs &&
+      (long long)num_seqs * a.Hkv >= kOrderMinItems && a.P > kAutoFourWaveBlocks * kBlockSize)
+    ao.order_seqs = num_seqs;
+  if (a.Pmax > 1 && a.split.shift == 0 && mfma && num_seqs >= 2 && num_seqs <= kOrderMaxSeqs)
     ao.order_seqs = num_seqs;
   switch (dtype) {
     case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, ao, l);
