@@ -283,6 +283,41 @@ def test_v1_many_sequences_in_longest_first_order(S, dtype, G):
         B.pa_set_mfma_variant(old)
 
 
+@pytest.mark.parametrize("dtype,G,D,P", [("bf16", 8, 128, 512), ("f16", 8, 256, 256),
+                                         ("bf16", 4, 128, 64)])
+def test_v2_compacted_order_matches_single_sequence_runs(dtype, G, D, P):
+    """V2 over several sequences takes the non-empty (sequence, head, partition) items in a
+    compacted order; every sequence's rows must be bitwise those of a V2 decode of that
+    sequence alone (one sequence: grid order) with the same kernel shape (the automatic
+    shape depends on the grid size), and empty sequences give exact zeros."""
+    ctx = [3000, 0, 1, 700, 5000, 16, 0, 1033]
+    w = small_workload(61 + D + P, ctx, Hq=2 * G, Hkv=2, D=D, dtype=dtype)
+    dev = upload(w)
+    ref = oracle.decode_attention(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                                  w.scale, w.dtype)
+    old = B.pa_get_mfma_variant()
+    B.pa_set_mfma_variant(1)
+    try:
+        with work_split(0):
+            say(f"v2 compacted dtype={dtype} G={G} D={D} P={P}")
+            out = run_path(w, dev, B.PA_PATH_V2, P)
+            check_close(to_f64(out), ref, f"v2 compacted P={P}")
+            assert torch.all(out[np.asarray(ctx) == 0] == 0)
+            for b in range(len(ctx)):
+                q1 = dev["q"][b:b + 1].clone()
+                one = torch.empty_like(q1)
+                bt1 = dev["block_tables"][b:b + 1].clone()
+                ws = torch.zeros(B.pa_workspace_bytes(q1, dev["k_cache"], bt1, 0, P),
+                                 dtype=torch.uint8, device="cuda")
+                B.pa_decode_ex(one, q1, dev["k_cache"], dev["v_cache"], bt1,
+                               dev["context_lens"][b:b + 1].clone(), w.scale, P,
+                               workspace=ws, path=B.PA_PATH_V2)
+                torch.cuda.synchronize()
+                assert torch.equal(one[0], out[b]), f"sequence {b}"
+    finally:
+        B.pa_set_mfma_variant(old)
+
+
 def test_identity_coded_values_select_exact_rows():
     """fp32 V = physical_block*16 + slot, q = 0: out is the mean of the selected codes."""
     ctx = [1000, 333, 16, 1]
