@@ -47,10 +47,11 @@ struct AttnArgs {
   int32_t P;                 // tokens per partition (multiple of 16)
   int32_t Pmax;              // partition-grid size
   Split split;
-  // > 0 (matrix-core kernel, no split): the number of sequences S, and work-groups do not
-  // take their item from the grid position.  V1 (Pmax == 1, four-wave shape): work-group
-  // z takes the sequence of rank z in longest-context-first order.  V2: work-group j takes
-  // the j-th non-empty (sequence, KV head, partition) item (see compact_item).
+  // > 0 (no split): the number of sequences S, and work-groups do not take their item
+  // from the grid position.  V1 (Pmax == 1, four-wave matrix-core shape): work-group z
+  // takes the sequence of rank z in longest-context-first order.  V2 (both kernels):
+  // work-group j takes the j-th non-empty (sequence, KV head, partition) item (see
+  // compact_item).
   int32_t order_seqs = 0;
 };
 constexpr int kOrderMaxSeqs = 512;  // longest-first orders (V1, prefill): at most this many sequences

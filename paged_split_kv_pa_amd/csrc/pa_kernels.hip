@@ -818,7 +818,8 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
   float* s_p = reinterpret_cast<float*>(smem + kQBytes);   // [kWaves][16][G]
   float* s_o = reinterpret_cast<float*>(smem);             // [kWaves-1][G*VE][64] after it
 
-  const Item it = grid_item(a);
+  Item it = grid_item(a);
+  if (a.order_seqs > 0 && a.Pmax > 1 && !compact_item(a, a.order_seqs, it)) return;
   const int g = it.g, b = it.b;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1414,14 +1415,15 @@ hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& 
   // trip): with 256 sequences of 256 tokens that doubled the step (23 -> 49 us), with
   // 2048 tokens it costs ~7 us when all lengths are equal, and with U{512..4096} lengths
   // it saves ~27 us.
-  // With V2 (Pmax > 1), several sequences and no split: the compacted item order.
+  // With V2 (Pmax > 1), several sequences and no split: the compacted item order (both
+  // attention kernels).
   AttnArgs ao = a;
   ao.order_seqs = 0;
   const bool mfma = kernel_for(dtype, group) == Kernel::kMfma;
   if (a.Pmax == 1 && a.split.shift == 0 && mfma && num_seqs <= kOrderMaxSeqs &&
       (long long)num_seqs * a.Hkv >= kOrderMinItems && a.P > kAutoFourWaveBlocks * kBlockSize)
     ao.order_seqs = num_seqs;
-  if (a.Pmax > 1 && a.split.shift == 0 && mfma && num_seqs >= 2 && num_seqs <= kOrderMaxSeqs)
+  if (a.Pmax > 1 && a.split.shift == 0 && num_seqs >= 2 && num_seqs <= kOrderMaxSeqs)
     ao.order_seqs = num_seqs;
   switch (dtype) {
     case PA_F32: return launch_attn_d<PA_F32>(head_dim, group, ao, l);

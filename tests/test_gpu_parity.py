@@ -284,7 +284,8 @@ def test_v1_many_sequences_in_longest_first_order(S, dtype, G):
 
 
 @pytest.mark.parametrize("dtype,G,D,P", [("bf16", 8, 128, 512), ("f16", 8, 256, 256),
-                                         ("bf16", 4, 128, 64)])
+                                         ("bf16", 4, 128, 64), ("f32", 4, 128, 512),
+                                         ("bf16", 2, 256, 256)])
 def test_v2_compacted_order_matches_single_sequence_runs(dtype, G, D, P):
     """V2 over several sequences takes the non-empty (sequence, head, partition) items in a
     compacted order; every sequence's rows must be bitwise those of a V2 decode of that
