@@ -15,11 +15,13 @@
 //     QK^T: v_mfma_f32_16x16x32_{bf16,f16}, A = the 16 keys of a block
 //     (rows = tokens), B = the group's queries (columns = heads, padded to
 //     16).  The result lands with column = head, rows = tokens, which is
-//     exactly the A-operand layout of PV: v_mfma_f32_16x16x16 with
-//     A = probabilities (rows = heads, k = tokens) and B = V (k = tokens).
-//     Each lane loads V rows as 16-byte runs of 8 columns and feeds column
-//     j of its run to PV instruction j, so no transpose through LDS is
-//     needed: column n of instruction j is head-dim index 8n + j.
+//     exactly the A-operand layout of PV: v_mfma_f32_16x16x32 with
+//     A = probabilities (rows = heads, k = tokens; each probability as a
+//     16-bit high part and a 16-bit low part in two k-slots) and B = V
+//     (k = tokens, each V row in both slots).  Each lane loads V rows as
+//     16-byte runs of 8 columns and feeds column j of its run to PV
+//     instruction j, so no transpose through LDS is needed: column n of
+//     instruction j is head-dim index 8n + j.
 //   * attn_valu_kernel (fp32, or G < 4): plain fp32 FMAs; the query group is
 //     staged in LDS and the probabilities of a block are exchanged through
 //     a per-wave LDS slot.
@@ -50,10 +52,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kWaves * 64;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -195,15 +194,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-template <bool BF>
-__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
-  if constexpr (BF)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
 // ---- leading kernel arguments ---------------------------------------------------------
@@ -627,8 +617,24 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = x[i] == kNegInf ? 0.f : exp2_fast(x[i] - m_ref);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const u32x2 pa = u32x2{pack2<DT>(pr[0], pr[1]), pack2<DT>(pr[2], pr[3])};
+    // P enters the PV product as a 16-bit high part plus a 16-bit low part (the rounding
+    // residual), stacked in the k dimension of one 16x16x32 instruction: k-slots
+    // 8 kg + i hold the high parts of tokens 4 kg + i, slots 8 kg + 4 + i their low parts,
+    // and the V operand repeats the same four rows in both halves.  p is thus carried to
+    // about 16 significant bits instead of 8 (bf16) or 11 (fp16), and the 16x16x32 form
+    // takes the same matrix-core cycles on gfx950 as the 16x16x16 one.  The exp-sum adds
+    // exactly the values the product uses (high plus rounded low part).
+    u32x4 pa;
+    {
+      const uint32_t h01 = pack2<DT>(pr[0], pr[1]), h23 = pack2<DT>(pr[2], pr[3]);
+      const float hf[4] = {half_lo<DT>(h01), half_hi<DT>(h01), half_lo<DT>(h23),
+                           half_hi<DT>(h23)};
+      const uint32_t l01 = pack2<DT>(pr[0] - hf[0], pr[1] - hf[1]);
+      const uint32_t l23 = pack2<DT>(pr[2] - hf[2], pr[3] - hf[3]);
+      l_run += ((hf[0] + half_lo<DT>(l01)) + (hf[1] + half_hi<DT>(l01))) +
+               ((hf[2] + half_lo<DT>(l23)) + (hf[3] + half_hi<DT>(l23)));
+      pa = u32x4{h01, h23, l01, l23};
+    }
     if (valid < kBlockSize) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -642,9 +648,9 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 bv = u32x2{__builtin_amdgcn_perm(vr[c][1][j >> 1], vr[c][0][j >> 1], sel),
-                               __builtin_amdgcn_perm(vr[c][3][j >> 1], vr[c][2][j >> 1], sel)};
-        O[8 * c + j] = mfma_16x16x16<kBF>(pa, bv, O[8 * c + j]);
+        const uint32_t v01 = __builtin_amdgcn_perm(vr[c][1][j >> 1], vr[c][0][j >> 1], sel);
+        const uint32_t v23 = __builtin_amdgcn_perm(vr[c][3][j >> 1], vr[c][2][j >> 1], sel);
+        O[8 * c + j] = mfma_16x16x32<kBF>(pa, u32x4{v01, v23, v01, v23}, O[8 * c + j]);
       }
   };
 

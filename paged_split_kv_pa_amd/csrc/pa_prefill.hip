@@ -31,6 +31,9 @@
 //                  accumulators of the two blocks are exactly the A operand (k-slot e of
 //                  lane group kg is key 16(2s + e/4) + 4kg + e%4); the B operand comes
 //                  from V in LDS through the gfx950 transposing read, in that key order.
+//                  P goes in as a 16-bit high part and a 16-bit low part (the rounding
+//                  residual), one product each, so that p keeps about 16 significant
+//                  bits; the row sums of P add exactly those values (on the VALU).
 // K and V have two LDS buffers each; a tile's K is written one phase before its first
 // QK^T and its V one phase before its first PV, from loads issued two phases earlier.
 
@@ -113,6 +116,32 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
+// sum over lanes l, l ^ 16, l ^ 32, l ^ 48, with the same half-swaps; the result is
+// bitwise the same in all four lanes (each adds the same two partial sums).
+__device__ __forceinline__ float sum_over_groups(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  uint32_t a0 = a[0], a1 = a[1];
+  asm("" : "+v"(a0), "+v"(a1));
+  u = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1));
+  const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  uint32_t b0 = b[0], b1 = b[1];
+  asm("" : "+v"(b0), "+v"(b1));
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+// The two 16-bit halves of a packed pair, widened to float.
+template <bool BF>
+__device__ __forceinline__ float unpack_lo(uint32_t w) {
+  if constexpr (BF) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <bool BF>
+__device__ __forceinline__ float unpack_hi(uint32_t w) {
+  if constexpr (BF) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -168,6 +197,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   __shared__ u32x4 s_k[2][kTile * ROW];
   __shared__ u32x4 s_v[2][kTile * ROW];
   __shared__ int s_pick;
+  // At head_dim 128 the query operands live in LDS, each wave's in lane order (16-byte
+  // reads, conflict-free): the two-part P of the PV product needs the registers.
+  constexpr bool kQLds = D == 128;
+  __shared__ u32x4 s_q[kQLds ? 8 : 1][kQLds ? CG * KK : 1][64];
 
   const int g = blockIdx.y;
   int b = blockIdx.z, xb = blockIdx.x;
@@ -203,7 +236,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // softmax works on raw dot products scaled by |scale| log2(e); a negative scale is
   // carried by flipping the sign of q (exact in 16-bit floats), so max(scale * s) is
   // |scale| * max of the flipped products.
-  u32x4 qf[CG][KK];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7]
+  u32x4 qf[CG][KK];  // [cg][kk]: Q[row r16][32kk + 8kg .. +7] (in LDS when kQLds)
   int qpos_col[CG];
   {
     const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -221,6 +254,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         qf[cg][kk] = (valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg)
                             : u32x4{0u, 0u, 0u, 0u}) ^ u32x4{flip, flip, flip, flip};
     }
+    if constexpr (kQLds) {
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s_q[w][cg * KK + kk][lane] = qf[cg][kk];
+    }
   }
   const float sl = fabsf(a.scale_log2);
   f32x4 O[CG][JD];
@@ -228,18 +267,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
     for (int j = 0; j < JD; ++j) O[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Row sums of P come from the matrix cores too: one more PV product per column group
-  // with an all-ones B operand leaves sum_k P[row][k] in every column, in the same
-  // row layout as O (and from the same bf16-rounded P as O).
-  f32x4 Lacc[CG];
+  // Row sums of P: lane (r16, kg) adds up the probabilities of query row r16 over its
+  // own keys (4 kg + i of every 16-key row block); the four lane groups are summed at
+  // the end.
+  float lsum[CG];
   float m_ref[CG];
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     m_ref[cg] = kNegInf;
-    Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[cg] = 0.f;
   }
-  const uint32_t one2 = kBF ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0
-  const u32x4 ones = {one2, one2, one2, one2};
 
   // ---- tile loads: thread tid moves XC chunks (lc, lc + 8, ...) of K and of V of tile row tid/8 ----
   // Loads are unconditional (a row outside the keys reads a valid dummy row and is
@@ -302,7 +339,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   __syncthreads();
 
   f32x4 S[4][CG];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
-  u32x4 P[CG][2];  // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1)
+  // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1), as the
+  // 16-bit high parts (P) and low parts (Pl).
+  u32x4 P[CG][2], Pl[CG][2];
 
   // S^T of tile t.
   auto qk = [&](int t) {
@@ -316,17 +355,22 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) S[rb][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int QR = kQLds ? CG : 0;  // query operand reads per k step
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 qk_op[CG];
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) qk_op[cg] = kQLds ? s_q[w][cg * KK + kk][lane] : qf[cg][kk];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg) S[rb][cg] = mfma32<kBF>(ka[kk][rb], qf[cg][kk], S[rb][cg]);
-    // the K reads of the next k step run under the current step's products
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int cg = 0; cg < CG; ++cg) S[rb][cg] = mfma32<kBF>(ka[kk][rb], qk_op[cg], S[rb][cg]);
+    }
+    // the K (and query) reads of the next k step run under the current step's products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + QR, 0);
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 + QR, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
@@ -349,22 +393,22 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int jd = 0; jd < JD; ++jd)
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg) O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
+        for (int cg = 0; cg < CG; ++cg) {
+          O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
+          O[cg][jd] = mfma32<kBF>(Pl[cg][st], vb[st][jd], O[cg][jd]);
+        }
+    // V reads (two per operand) run two operands ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg) Lacc[cg] = mfma32<kBF>(P[cg][st], ones, Lacc[cg]);
-    }
-    // V reads (two per operand) run four operands ahead of the products that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * JD - 4; ++k) {
+    for (int k = 0; k < 2 * JD - 2; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, CG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * CG, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6 * CG, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
   };
   // Softmax of tile t: row max (masked keys become -inf on diagonal tiles, where S then
   // holds scaled logits), the rescale of O when a row max grows past the slack, and P.
@@ -405,8 +449,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         for (int j = 0; j < JD; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
+        lsum[cg] *= alpha;  // this lane's sums are of row r16, the row alpha belongs to
       }
     }
     // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
@@ -416,13 +459,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
       const float nm = -m_ref[cg];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float p[2][4];
+        float p[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[h][i] = exp2_fast(fmaf(S[2 * st + h][cg][i], fs, nm));
-        P[cg][st] = u32x4{pack2<kBF>(p[0][0], p[0][1]), pack2<kBF>(p[0][2], p[0][3]),
-                          pack2<kBF>(p[1][0], p[1][1]), pack2<kBF>(p[1][2], p[1][3])};
+          for (int i = 0; i < 4; ++i) p[4 * h + i] = exp2_fast(fmaf(S[2 * st + h][cg][i], fs, nm));
+        uint32_t hw[4], lw[4];
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hw[e] = pack2<kBF>(p[2 * e], p[2 * e + 1]);
+          const float h0 = unpack_lo<kBF>(hw[e]), h1 = unpack_hi<kBF>(hw[e]);
+          lw[e] = pack2<kBF>(p[2 * e] - h0, p[2 * e + 1] - h1);
+          part += (h0 + unpack_lo<kBF>(lw[e])) + (h1 + unpack_hi<kBF>(lw[e]));
+        }
+        lsum[cg] += part;
+        P[cg][st] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        Pl[cg][st] = u32x4{lw[0], lw[1], lw[2], lw[3]};
       }
     }
   };
@@ -484,9 +537,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
+    const float lrow = sum_over_groups(lsum[cg]);  // row r16's sum, in every lane group
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = Lacc[cg][i];
+      const float li = __shfl(lrow, 4 * kg + i);
       const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
       const int pos = p0 + row / G;
       if (pos >= L) continue;
