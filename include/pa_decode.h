@@ -22,14 +22,21 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * All tensor pointers are DEVICE pointers, owned by the caller; the library
- * never frees or retains them past the call.  Layouts are dense, row-major:
+ * never frees or retains them past the call.  Logical shapes:
  *   q, out          [S, Hq, D]          element type = dims->dtype
  *   k_cache,v_cache [NB, Hkv, 16, D]    element type = dims->dtype
  *   block_tables    [S, MB]   int32     physical block ids into the pool
  *   context_lens    [S]       int32     tokens cached per sequence
+ * Memory layout: row-major by default; the stride fields of pa_dims_t describe
+ * strided views (q or out inside a fused QKV / output buffer, K and V
+ * interleaved per block, a block table that is a column slice of a wider one).
+ * The innermost (head-dim) stride must be 1 and each 16-token block of one KV
+ * head must be contiguous ([16, D] dense).
  * Token t of sequence b is slot (t % 16) of physical block
  * block_tables[b][t / 16].  Query head h reads KV head h / (Hq / Hkv).
- * Every tensor pointer must be 16-byte aligned (PA_ERR_ALIGN otherwise).
+ * q, out, k_cache and v_cache must be 16-byte aligned, and so must every q / out
+ * row and every cache block (strides times element size multiples of 16 bytes);
+ * block_tables and context_lens 4-byte aligned.  PA_ERR_ALIGN otherwise.
  * out must not alias any input; it is fully overwritten (a sequence with no
  * tokens gets 0).  out takes the element type of q, rounded to nearest even
  * from the fp32 accumulator.
@@ -61,12 +68,13 @@ typedef enum pa_status {
   PA_ERR_NULL = -1,        /* a required pointer is NULL */
   PA_ERR_DTYPE = -2,       /* unknown element type */
   PA_ERR_SHAPE = -3,       /* inconsistent or non-positive sizes */
-  PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+  PA_ERR_ALIGN = -4,       /* a tensor pointer or row is not 16-byte aligned */
   PA_ERR_PARTITION = -5,   /* partition_size <= 0 or not a multiple of block_size */
   PA_ERR_UNSUPPORTED = -6, /* valid but not built: D, block_size, G, too many partitions */
   PA_ERR_WORKSPACE = -7,   /* caller workspace NULL or smaller than pa_workspace_bytes() */
   PA_ERR_HIP = -8,         /* a HIP runtime call or kernel launch failed */
-  PA_ERR_INTERNAL = -9
+  PA_ERR_INTERNAL = -9,
+  PA_ERR_STRIDE = -10      /* a stride the kernels cannot take (innermost != 1, overlap) */
 } pa_status_t;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
@@ -74,7 +82,21 @@ typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
 /* Decode-path selector for pa_decode_ex. */
 enum { PA_PATH_AUTO = 0, PA_PATH_V1 = 1, PA_PATH_V2 = 2 };
 
-/* Problem sizes, passed by pointer to every entry point.  Plain integers. */
+/* Problem sizes and strides, passed by pointer to every entry point.  Plain
+ * integers.  Strides are in elements of the tensor's own type; 0 selects the
+ * row-major value (given in brackets), so a zero-initialised stride block
+ * describes dense tensors.  Rules (checked on the host, before any HIP call):
+ *   q / out: *_stride_dim must be 0 or 1 (PA_ERR_STRIDE otherwise); the head and
+ *     sequence strides must be positive and below 2^31, with every row start
+ *     16-byte aligned (PA_ERR_ALIGN).  out rows must not overlap:
+ *     out_stride_head >= D and out_stride_seq >= (Hq - 1) * out_stride_head + D
+ *     (PA_ERR_STRIDE).  q rows may overlap (q is only read).
+ *   kv_stride_block: distance between consecutive blocks of k_cache and of
+ *     v_cache (the same for both), >= Hkv*16*D, 16-byte multiple; within a block
+ *     the layout is [Hkv, 16, D] dense.  Setting it to 2*Hkv*16*D describes K and V
+ *     interleaved per block ([NB, 2, Hkv, 16, D] with k_cache = &kv[0][0] and
+ *     v_cache = &kv[0][1]).
+ *   bt_stride_seq: int32 entries between block-table rows, >= MB. */
 typedef struct pa_dims {
   int32_t num_seqs;           /* S   (0 is allowed: nothing to do) */
   int32_t num_q_heads;        /* Hq */
@@ -84,6 +106,14 @@ typedef struct pa_dims {
   int32_t num_blocks;         /* NB: blocks in the KV pool */
   int32_t max_blocks_per_seq; /* MB: block_tables row length */
   int32_t dtype;              /* pa_dtype_t of q, k_cache, v_cache and out */
+  int64_t q_stride_seq;       /* [Hq*D] */
+  int64_t q_stride_head;      /* [D] */
+  int64_t q_stride_dim;       /* [1]; must be 0 or 1 */
+  int64_t out_stride_seq;     /* [Hq*D] */
+  int64_t out_stride_head;    /* [D] */
+  int64_t out_stride_dim;     /* [1]; must be 0 or 1 */
+  int64_t kv_stride_block;    /* [Hkv*16*D] */
+  int64_t bt_stride_seq;      /* [MB] */
 } pa_dims_t;
 
 /*

@@ -5,11 +5,15 @@ a ``pa_dims_t``; every step of the computation runs in the library's HIP
 kernels.  The functions keep the C names.  There is no fallback: if the
 library is missing or a call fails, a ``PaError`` is raised.
 
-Tensors (all on the same CUDA/HIP device, contiguous):
-  q, out           [S, Hq, D]        float32 / float16 / bfloat16
-  k_cache, v_cache [NB, Hkv, 16, D]  same dtype as q
-  block_tables     [S, MB]           int32
-  context_lens     [S]               int32
+Tensors (all on the same CUDA/HIP device):
+  q, out           [S, Hq, D]        float32 / float16 / bfloat16; any sequence and head
+                                     strides (e.g. views into a fused QKV buffer), head-dim
+                                     stride 1
+  k_cache, v_cache [NB, Hkv, 16, D]  same dtype as q; each block [Hkv, 16, D] dense, any
+                                     (common) block stride
+  block_tables     [S, MB]           int32; any row stride, entries contiguous
+  context_lens     [S]               int32, contiguous
+The strides travel in pa_dims_t; the library validates them (PA_ERR_STRIDE, PA_ERR_ALIGN).
 """
 import ctypes
 import os
@@ -20,7 +24,9 @@ LIB_PATH = os.path.join(_HERE, "lib", "libpa_decode.so")
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
                 -4: "PA_ERR_ALIGN", -5: "PA_ERR_PARTITION", -6: "PA_ERR_UNSUPPORTED",
-                -7: "PA_ERR_WORKSPACE", -8: "PA_ERR_HIP", -9: "PA_ERR_INTERNAL"}
+                -7: "PA_ERR_WORKSPACE", -8: "PA_ERR_HIP", -9: "PA_ERR_INTERNAL",
+                -10: "PA_ERR_STRIDE"}
+PA_ERR_STRIDE = -10
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PATH_AUTO, PA_PATH_V1, PA_PATH_V2 = 0, 1, 2
 
@@ -35,7 +41,11 @@ class PaDims(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q_stride_seq", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+                ("q_stride_dim", ctypes.c_int64), ("out_stride_seq", ctypes.c_int64),
+                ("out_stride_head", ctypes.c_int64), ("out_stride_dim", ctypes.c_int64),
+                ("kv_stride_block", ctypes.c_int64), ("bt_stride_seq", ctypes.c_int64)]
 
 
 class PaPrefillDims(ctypes.Structure):
@@ -119,24 +129,45 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
-def dims_of(q, k_cache, block_tables):
-    """pa_dims_t from tensor shapes (q [S,Hq,D], k_cache [NB,Hkv,bs,D], table [S,MB])."""
+def dims_of(q, k_cache, block_tables, out=None, v_cache=None):
+    """pa_dims_t from tensor shapes and strides (q [S,Hq,D], k_cache [NB,Hkv,bs,D], table
+    [S,MB]; out and v_cache, when given, for their strides)."""
     if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
         raise PaError(-3, "q must be 3-D, k_cache 4-D and block_tables 2-D")
     S, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_cache.shape
     if Dk != D:
         raise PaError(-3, f"head_dim of q ({D}) and k_cache ({Dk}) differ")
-    return PaDims(S, Hq, Hkv, D, bs, NB, block_tables.shape[1], _dtype_code(q))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t is not None and tuple(t.stride()[1:]) != (bs * D, D, 1) and t.numel() > 0:
+            raise PaError(PA_ERR_STRIDE, f"{name}: every block must be a dense [Hkv, 16, D] "
+                                         f"array (strides {tuple(t.stride())})")
+    if v_cache is not None and v_cache.stride(0) != k_cache.stride(0):
+        raise PaError(PA_ERR_STRIDE, "k_cache and v_cache must have the same block stride")
+    if block_tables.stride(1) != 1 and block_tables.shape[1] > 1:
+        raise PaError(PA_ERR_STRIDE, "block_tables rows must be contiguous")
+    d = PaDims(S, Hq, Hkv, D, bs, NB, block_tables.shape[1], _dtype_code(q))
+
+    def st(t, i):  # the stride of a size-1 dimension is never used: 0 (the default)
+        return 0 if t.shape[i] == 1 else t.stride(i)
+    d.q_stride_seq, d.q_stride_head, d.q_stride_dim = st(q, 0), st(q, 1), q.stride(2)
+    if out is not None:
+        d.out_stride_seq, d.out_stride_head, d.out_stride_dim = st(out, 0), st(out, 1), \
+            out.stride(2)
+    d.kv_stride_block = st(k_cache, 0)
+    d.bt_stride_seq = st(block_tables, 0)
+    return d
 
 
-def _ptr(t, name, dtype=None):
+def _ptr(t, name, dtype=None, strided=False):
+    """Device address of t; strided tensors are described to the library by their
+    strides (pa_dims_t), others must be contiguous."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise PaError(-1, f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise PaError(-1, f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if not strided and not t.is_contiguous():
         raise PaError(-3, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise PaError(-2, f"{name} must be {dtype}, got {t.dtype}")
@@ -164,15 +195,16 @@ def _tensors(out, q, k_cache, v_cache, block_tables, context_lens):
     if context_lens.dim() != 1 or context_lens.shape[0] != q.shape[0] or \
             block_tables.shape[0] != q.shape[0]:
         raise PaError(-3, "block_tables and context_lens need one row per sequence")
-    return (_ptr(out, "out"), _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
-            _ptr(block_tables, "block_tables", torch.int32),
+    return (_ptr(out, "out", strided=True), _ptr(q, "q", strided=True),
+            _ptr(k_cache, "k_cache", strided=True), _ptr(v_cache, "v_cache", strided=True),
+            _ptr(block_tables, "block_tables", torch.int32, strided=True),
             _ptr(context_lens, "context_lens", torch.int32))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size=512,
               stream=None):
     """One decode step; path by context bound; library-owned workspace."""
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     _check(lib().pa_decode(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
                            _stream(stream)))
@@ -196,7 +228,7 @@ def _ws(workspace):
 def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  partition_size=512, stream=None, workspace=None, max_context_len=0,
                  path=PA_PATH_AUTO):
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     wp, wb = _ws(workspace)
     _check(lib().pa_decode_ex(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
@@ -208,7 +240,7 @@ def pa_decode_profiled(out, q, k_cache, v_cache, block_tables, context_lens, sca
                        partition_size=512, stream=None, workspace=None, max_context_len=0,
                        path=PA_PATH_AUTO, start_event=None, stop_event=None):
     """pa_decode_ex plus runtime timestamps (hipEvent_t handles) of the attention kernel."""
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     wp, wb = _ws(workspace)
     _check(lib().pa_decode_profiled(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
@@ -219,7 +251,7 @@ def pa_decode_profiled(out, q, k_cache, v_cache, block_tables, context_lens, sca
 
 def pa_v2_partition(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
                     partition_size=512, max_context_len=0, stream=None):
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     wp, wb = _ws(workspace)
     _check(lib().pa_v2_partition(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
@@ -230,9 +262,9 @@ def pa_v2_partition(out, q, k_cache, v_cache, block_tables, context_lens, scale,
 def pa_v2_reduce(out, q, k_cache, block_tables, context_lens, workspace, partition_size=512,
                  max_context_len=0, stream=None):
     import torch
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out)
     wp, wb = _ws(workspace)
-    _check(lib().pa_v2_reduce(ctypes.byref(d), _ptr(out, "out"),
+    _check(lib().pa_v2_reduce(ctypes.byref(d), _ptr(out, "out", strided=True),
                               _ptr(context_lens, "context_lens", torch.int32),
                               int(partition_size), int(max_context_len), wp, wb,
                               _stream(stream)))
@@ -241,7 +273,7 @@ def pa_v2_reduce(out, q, k_cache, block_tables, context_lens, workspace, partiti
 
 def pa_v1(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len=0,
           stream=None):
-    d = dims_of(q, k_cache, block_tables)
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     _check(lib().pa_v1(ctypes.byref(d), *ptrs, float(scale), int(max_context_len),
                        _stream(stream)))

@@ -68,6 +68,8 @@ int element_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
 // Sizes derived from validated dims.
 struct Plan {
   int S, Hq, Hkv, D, G, NB, MB;
+  // Strides in elements (block-table entries for bt_ss), zeros of pa_dims_t resolved.
+  int64_t q_ss, q_sh, o_ss, o_sh, kv_sb, bt_ss;
   int64_t ctx_bound;  // planning bound on every context length
   int32_t P;          // partition size used by the kernels
   int64_t Pmax;       // partition-grid size
@@ -125,10 +127,52 @@ pa_status_t check_dims(const pa_dims_t* d) {
   return ok();
 }
 
+// Strides of pa_dims_t (0 = row-major) resolved and checked against what the kernels take:
+// innermost stride 1, 16-byte aligned rows and blocks, out rows that do not overlap,
+// values the kernels' 32-bit fields hold.
+pa_status_t resolve_strides(const pa_dims_t* d, Plan* pl) {
+  const int64_t D = d->head_dim, Hq = d->num_q_heads;
+  const int64_t esz = element_bytes(d->dtype);
+  if ((d->q_stride_dim != 0 && d->q_stride_dim != 1) ||
+      (d->out_stride_dim != 0 && d->out_stride_dim != 1))
+    return fail(PA_ERR_STRIDE, "the head-dim stride of q and out must be 1 (got %lld and %lld)",
+                (long long)d->q_stride_dim, (long long)d->out_stride_dim);
+  auto pick = [](int64_t v, int64_t dense) { return v == 0 ? dense : v; };
+  pl->q_sh = pick(d->q_stride_head, D);
+  pl->q_ss = pick(d->q_stride_seq, Hq * D);
+  pl->o_sh = pick(d->out_stride_head, D);
+  pl->o_ss = pick(d->out_stride_seq, Hq * D);
+  pl->kv_sb = pick(d->kv_stride_block, (int64_t)d->num_kv_heads * pa::kBlockSize * D);
+  pl->bt_ss = pick(d->bt_stride_seq, d->max_blocks_per_seq);
+  const int64_t lim = 0x7fffffff;
+  if (pl->q_sh < 0 || pl->q_ss < 0 || pl->o_sh < 0 || pl->o_ss < 0 || pl->kv_sb < 0 ||
+      pl->bt_ss < 0)
+    return fail(PA_ERR_STRIDE, "strides must not be negative");
+  if (pl->q_sh > lim || pl->q_ss > lim || pl->bt_ss > lim)
+    return fail(PA_ERR_UNSUPPORTED, "q strides and the block-table row stride must be below 2^31");
+  if (pl->o_sh < D || pl->o_ss < (Hq - 1) * pl->o_sh + D)
+    return fail(PA_ERR_STRIDE,
+                "out rows overlap (out_stride_head %lld must be >= %lld and out_stride_seq %lld "
+                ">= %lld)", (long long)pl->o_sh, (long long)D, (long long)pl->o_ss,
+                (long long)((Hq - 1) * pl->o_sh + D));
+  if (pl->kv_sb < (int64_t)d->num_kv_heads * pa::kBlockSize * D)
+    return fail(PA_ERR_STRIDE, "kv_stride_block %lld is smaller than a block (%lld elements)",
+                (long long)pl->kv_sb, (long long)d->num_kv_heads * pa::kBlockSize * D);
+  if (pl->bt_ss < d->max_blocks_per_seq)
+    return fail(PA_ERR_STRIDE, "bt_stride_seq %lld is smaller than max_blocks_per_seq %d",
+                (long long)pl->bt_ss, d->max_blocks_per_seq);
+  if ((pl->q_sh * esz) % 16 || (pl->q_ss * esz) % 16 || (pl->o_sh * esz) % 16 ||
+      (pl->o_ss * esz) % 16 || (pl->kv_sb * esz) % 16)
+    return fail(PA_ERR_ALIGN, "q / out rows and cache blocks must start on 16-byte boundaries "
+                "(strides times %lld bytes must be multiples of 16)", (long long)esz);
+  return ok();
+}
+
 pa_status_t make_plan(const pa_dims_t* d, int64_t max_context_len, int32_t partition_size,
                       bool need_partition, Plan* pl) {
   pa_status_t st = check_dims(d);
   if (st != PA_OK) return st;
+  if ((st = resolve_strides(d, pl)) != PA_OK) return st;
   pl->S = d->num_seqs;
   pl->Hq = d->num_q_heads;
   pl->Hkv = d->num_kv_heads;
@@ -260,9 +304,10 @@ pa_status_t check_tensors(const void* out, const void* q, const void* k, const v
   if (!out || !q || !k || !v || !bt || !ctx)
     return fail(PA_ERR_NULL, "a tensor pointer is NULL (out=%p q=%p k=%p v=%p bt=%p ctx=%p)", out,
                 q, k, v, (const void*)bt, (const void*)ctx);
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bt) ||
-      !aligned16(ctx))
-    return fail(PA_ERR_ALIGN, "every tensor pointer must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(PA_ERR_ALIGN, "out, q, k_cache and v_cache must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(bt) | reinterpret_cast<uintptr_t>(ctx)) & 3u)
+    return fail(PA_ERR_ALIGN, "block_tables and context_lens must be 4-byte aligned");
   return ok();
 }
 
@@ -292,6 +337,12 @@ pa::AttnArgs attn_args(const Plan& pl, void* out, const void* q, const void* k, 
   a.v = v;
   a.bt = bt;
   a.ctx = ctx;
+  a.q_ss = (int32_t)pl.q_ss;
+  a.q_sh = (int32_t)pl.q_sh;
+  a.bt_ss = (int32_t)pl.bt_ss;
+  a.o_ss = pl.o_ss;
+  a.o_sh = pl.o_sh;
+  a.kv_sb = pl.kv_sb;
   char* base = static_cast<char*>(ws);
   a.tmp_out = base ? reinterpret_cast<float*>(base + pl.off_tmp) : nullptr;
   a.max_logits = base ? reinterpret_cast<float*>(base + pl.off_max) : nullptr;
@@ -321,6 +372,8 @@ pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const i
   pa::ReduceArgs r;
   const char* base = static_cast<const char*>(ws);
   r.out = out;
+  r.o_ss = pl.o_ss;
+  r.o_sh = pl.o_sh;
   r.ctx = ctx;
   r.tmp_out = reinterpret_cast<const float*>(base + pl.off_tmp);
   r.max_logits = reinterpret_cast<const float*>(base + pl.off_max);
@@ -578,8 +631,8 @@ pa_status_t pa_v2_reduce(const pa_dims_t* dims, void* out, const int32_t* contex
   if (st != PA_OK) return st;
   if (pl.S == 0) return ok();
   if (!out || !context_lens) return fail(PA_ERR_NULL, "out or context_lens is NULL");
-  if (!aligned16(out) || !aligned16(context_lens))
-    return fail(PA_ERR_ALIGN, "every tensor pointer must be 16-byte aligned");
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return fail(PA_ERR_ALIGN, "out must be 16-byte aligned and context_lens 4-byte aligned");
   if (!workspace || workspace_bytes < pl.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu needed", workspace,
                 workspace_bytes, pl.ws_bytes);

@@ -31,14 +31,17 @@ struct Split {
   float* piece_sum = nullptr;   // [slots][G]
 };
 
-// Arguments of the attention kernel (phase 1 and V1 share it).
+// Arguments of the attention kernel (phase 1 and V1 share it).  Strides are in elements
+// (block-table entries for bt_ss); all are validated on the host.
 struct AttnArgs {
-  void* out;                 // [S, Hq, D] element type of q
-  const void* q;             // [S, Hq, D]
-  const void* k;             // [NB, Hkv, 16, D]
-  const void* v;             // [NB, Hkv, 16, D]
-  const int32_t* bt;         // [S, MB]
+  void* out;                 // [S, Hq, D] element type of q, strides (o_ss, o_sh, 1)
+  const void* q;             // [S, Hq, D], strides (q_ss, q_sh, 1)
+  const void* k;             // [NB, Hkv, 16, D], block stride kv_sb, dense within a block
+  const void* v;             // [NB, Hkv, 16, D], block stride kv_sb
+  const int32_t* bt;         // [S, MB], row stride bt_ss
   const int32_t* ctx;        // [S]
+  int32_t q_ss, q_sh, bt_ss;
+  int64_t o_ss, o_sh, kv_sb;
   float* tmp_out;            // [S, Hq, Pmax, D] (unused when Pmax == 1)
   float* max_logits;         // [S, Hq, Pmax]
   float* exp_sums;           // [S, Hq, Pmax]
@@ -58,7 +61,8 @@ constexpr int kOrderMaxSeqs = 512;  // longest-first orders (V1, prefill): at mo
 
 // Arguments of the phase-2 (cross-partition) kernel.
 struct ReduceArgs {
-  void* out;
+  void* out;                 // [S, Hq, D], strides (o_ss, o_sh, 1)
+  int64_t o_ss, o_sh;
   const int32_t* ctx;
   const float* tmp_out;
   const float* max_logits;

@@ -203,31 +203,38 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // preloading (gfx950): the hardware places these leading scalar arguments in scalar
 // registers at wave launch, so a work-group issues those loads without first waiting for
 // a load of its argument block.  A by-value struct argument is never preloaded.
+// The hardware preloads at most 14 argument dwords (16 user registers, two of which hold
+// the argument-block address): three pointers and eight integers, two of them packed
+// (the number of KV heads with the sequence-order count, the split's first cut item with
+// its piece shift).
 #define PA_ATTN_LEAD_PARAMS                                                                \
   const int32_t *lead_ctx, const int32_t *lead_bt, const void *lead_q, int32_t lead_Pmax, \
-      int32_t lead_Hkv, int32_t lead_MB, int32_t lead_P, int32_t lead_Hq,                 \
-      int32_t lead_shift, int32_t lead_first, int32_t lead_order
+      int32_t lead_hkv_order, int32_t lead_MB, int32_t lead_P, int32_t lead_q_sh,         \
+      int32_t lead_first_shift, int32_t lead_q_ss, int32_t lead_bt_ss
 
 __device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, const int32_t* bt,
-                                              const void* q, int32_t Pmax, int32_t Hkv,
-                                              int32_t MB, int32_t P, int32_t Hq, int32_t shift,
-                                              int32_t first, int32_t order) {
+                                              const void* q, int32_t Pmax, int32_t hkv_order,
+                                              int32_t MB, int32_t P, int32_t q_sh,
+                                              int32_t first_shift, int32_t q_ss,
+                                              int32_t bt_ss) {
   a.ctx = ctx;
   a.bt = bt;
   a.q = q;
   a.Pmax = Pmax;
-  a.Hkv = Hkv;
+  a.Hkv = hkv_order & 0xffff;
+  a.order_seqs = hkv_order >> 16;
   a.MB = MB;
   a.P = P;
-  a.Hq = Hq;
-  a.split.shift = shift;
-  a.split.first = first;
-  a.order_seqs = order;
+  a.q_sh = q_sh;
+  a.split.shift = first_shift & 15;
+  a.split.first = first_shift >> 4;
+  a.q_ss = q_ss;
+  a.bt_ss = bt_ss;
   return a;
 }
-#define PA_ATTN_APPLY_LEAD(args)                                                        \
-  with_lead(args, lead_ctx, lead_bt, lead_q, lead_Pmax, lead_Hkv, lead_MB, lead_P, lead_Hq, \
-            lead_shift, lead_first, lead_order)
+#define PA_ATTN_APPLY_LEAD(args)                                                           \
+  with_lead(args, lead_ctx, lead_bt, lead_q, lead_Pmax, lead_hkv_order, lead_MB, lead_P,   \
+            lead_q_sh, lead_first_shift, lead_q_ss, lead_bt_ss)
 
 // Consumes the context length and one field of each 64-byte line of the argument
 // struct (output, K/V bases, pool size and scale), so that their scalar loads are issued
@@ -236,7 +243,7 @@ __device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, co
 // field load only where the field is first used, every one a separate wait.
 #define PA_PIN_EARLY_SCALARS(a, n_ctx)                                                   \
   asm volatile("" ::"s"(n_ctx), "s"((a).out), "s"((a).k), "s"((a).v), "s"((a).NB),       \
-               "s"((a).scale_log2))
+               "s"((a).scale_log2), "s"((a).kv_sb))
 
 // ---- work-group set-up shared by both attention kernels ------------------------------
 // The grid item of this work-group (see Split): partition p of KV head g of sequence b,
@@ -417,13 +424,22 @@ __device__ __forceinline__ void partial_rows(const AttnArgs& a, const Item& it, 
   }
 }
 
+// Element offsets of row (sequence b, query head h) of q and of out.
+__device__ __forceinline__ size_t q_offset(const AttnArgs& a, int b, int h) {
+  return (size_t)b * (uint32_t)a.q_ss + (size_t)h * (uint32_t)a.q_sh;
+}
+__device__ __forceinline__ size_t out_offset(const AttnArgs& a, int b, int h) {
+  return (size_t)b * (size_t)a.o_ss + (size_t)h * (size_t)a.o_sh;
+}
+
 // A sequence with no cached tokens attends to nothing: its output is 0.
 template <int DT, int D, int G>
 __device__ __forceinline__ void write_zero_group(const AttnArgs& a, int b, int g) {
-  const size_t base = ((size_t)b * a.Hq + (size_t)g * G) * D;
   const float z[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int idx = threadIdx.x * 4; idx < G * D; idx += blockDim.x * 4)
-    store_out<DT, 4>(a.out, base + idx, z);
+  for (int idx = threadIdx.x * 4; idx < G * D; idx += blockDim.x * 4) {
+    const int h = idx / D, d = idx - h * D;
+    store_out<DT, 4>(a.out, out_offset(a, b, g * G + h) + d, z);
+  }
 }
 
 // =======================================================================================
@@ -496,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   const int blk0 = tok0n / kBlockSize;
   const int nblk_nom = min(lenn / kBlockSize, a.MB - blk0);
   const int kcount_nom = w < nblk_nom ? (nblk_nom - w + NW - 1) / NW : 0;
-  const int32_t* btrow = a.bt + (size_t)b * a.MB + blk0;
+  const int32_t* btrow = a.bt + (size_t)b * (uint32_t)a.bt_ss + blk0;
   int btv = lane < min(64, kcount_nom) ? btrow[w + NW * lane] : 0;  // first 64 block ids
 
   // Query operand: lane (r16, kg) holds head r16, columns 32*kk + 8*kg .. +7 (zero rows
@@ -505,8 +521,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   // head; wave 0 stores, zeros for the padding) so that the prologue is straight-line and
   // the compiler can neither sink them behind the context-length test nor put a wait
   // ahead of them.
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                         ((size_t)b * a.Hq + (size_t)g * G + min(r16, G - 1)) * D;
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + q_offset(a, b, g * G + min(r16, G - 1));
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kg);
@@ -527,7 +542,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
 
   const size_t hstride = (size_t)kBlockSize * D;
-  const size_t bstride = (size_t)a.Hkv * hstride;
+  const size_t bstride = (size_t)a.kv_sb;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (size_t)g * hstride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + (size_t)g * hstride;
 
@@ -737,7 +752,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
     float fac[NW], Mt, L;
     head_stats(h, fac, Mt, L);
     const float linv = 1.f / L;
-    const size_t qh = (size_t)b * a.Hq + (size_t)g * G + h;
+    const size_t orow = out_offset(a, b, g * G + h);
     float *po, *pm, *ps;
     partial_rows<G, D>(a, it, h, po, pm, ps);
 #pragma unroll
@@ -753,7 +768,7 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
       }
       const int d0 = 128 * c + 8 * r16;
       if (single)
-        store_out<DT, 8>(a.out, qh * D + d0, vals);
+        store_out<DT, 8>(a.out, orow + d0, vals);
       else
         store_f32<8>(po + d0, vals);
     }
@@ -840,7 +855,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
   const int blk0 = tok0n / kBlockSize;
   const int nblk_nom = min(lenn / kBlockSize, a.MB - blk0);
   const int kcount_nom = w < nblk_nom ? (nblk_nom - w + kWaves - 1) / kWaves : 0;
-  const int32_t* btrow = a.bt + (size_t)b * a.MB + blk0;
+  const int32_t* btrow = a.bt + (size_t)b * (uint32_t)a.bt_ss + blk0;
   int btv = lane < min(64, kcount_nom) ? btrow[w + kWaves * lane] : 0;
 
   // Stage the head group's queries, pre-multiplied by scale*log2(e), as fp32 (all loads
@@ -850,7 +865,8 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
 #pragma unroll
   for (int i = 0; i < kQIter; ++i) {
     const int idx = min(tid + i * kThreads, G * D - 1);
-    const size_t src = ((size_t)b * a.Hq + (size_t)g * G) * D + idx;
+    const int hh = idx / D;
+    const size_t src = q_offset(a, b, g * G + hh) + (idx - hh * D);
     if constexpr (DT == PA_F32) qv[i] = static_cast<const float*>(a.q)[src];
     else qv[i] = half_lo<DT>(static_cast<const uint16_t*>(a.q)[src]);
   }
@@ -869,7 +885,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
   const int kcount = w < pt.nblk ? (pt.nblk - w + kWaves - 1) / kWaves : 0;
   asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
   const size_t hstride = (size_t)kBlockSize * ROWB;   // bytes per (block, head)
-  const size_t bstride = (size_t)a.Hkv * hstride;
+  const size_t bstride = (size_t)a.kv_sb * ES;        // bytes per block
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + (size_t)g * hstride;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + (size_t)g * hstride;
   __syncthreads();
@@ -1039,9 +1055,8 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
         o += fac[ww] * s_o[((ww - 1) * G * VE + h * VE + e) * 64 + lane];
       vals[e] = o * linv;
     }
-    const size_t qh = (size_t)b * a.Hq + (size_t)g * G + h;
     if (single) {
-      store_out<DT, VE>(a.out, qh * D + lane * VE, vals);
+      store_out<DT, VE>(a.out, out_offset(a, b, g * G + h) + lane * VE, vals);
     } else {
       float *po, *pm, *ps;
       partial_rows<G, D>(a, it, h, po, pm, ps);
@@ -1170,7 +1185,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
   int n = a.ctx[b];
   // The output address and the table shape load within the same round trip (they are
   // not used before it ends).
-  asm volatile("" ::"s"(n), "s"(a.out), "s"(a.MB), "s"(a.P));
+  asm volatile("" ::"s"(n), "s"(a.out), "s"(a.MB), "s"(a.P), "s"(a.o_ss), "s"(a.o_sh));
   const int cap = a.MB * kBlockSize;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   int nparts = (n + a.P - 1) / a.P;
@@ -1251,7 +1266,10 @@ __global__ void __launch_bounds__(256) reduce_kernel(PA_REDUCE_LEAD_PARAMS,
     const f32x4 o = (s_acc[0][d4] + s_acc[1][d4]) + (s_acc[2][d4] + s_acc[3][d4]);
     const float inv = 1.f / total;
     const float vals[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-    store_out<DT, 4>(a.out, (size_t)bh * D + chunk * kReduceCols + tid * 4, vals);
+    store_out<DT, 4>(a.out,
+                     (size_t)b * (size_t)a.o_ss + (size_t)hq * (size_t)a.o_sh +
+                         chunk * kReduceCols + tid * 4,
+                     vals);
   }
 }
 
@@ -1305,8 +1323,8 @@ struct Launch {
 template <typename K>
 void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
   hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a.ctx, a.bt, a.q,
-                        a.Pmax, a.Hkv, a.MB, a.P, a.Hq, a.split.shift, a.split.first,
-                        a.order_seqs, a);
+                        a.Pmax, a.Hkv | (a.order_seqs << 16), a.MB, a.P, a.q_sh,
+                        (a.split.first << 4) | a.split.shift, a.q_ss, a.bt_ss, a);
 }
 
 template <int DT, int D, int G>

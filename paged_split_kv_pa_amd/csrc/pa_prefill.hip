@@ -392,15 +392,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         const u32x2 hi = lds_read_tr(src + 16 * ROW * 16);
         vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
+    // Per pair of 16-column blocks: the high-part products of both blocks and every
+    // column group, then the low-part ones, so a product never waits for the one just
+    // issued on the same accumulator.
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int jd = 0; jd < JD; ++jd)
+      for (int jd = 0; jd < JD; jd += 2) {
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg) {
-          O[cg][jd] = mfma32<kBF>(P[cg][st], vb[st][jd], O[cg][jd]);
-          O[cg][jd] = mfma32<kBF>(Pl[cg][st], vb[st][jd], O[cg][jd]);
-        }
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int cg = 0; cg < CG; ++cg)
+            O[cg][jd + jj] = mfma32<kBF>(P[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int cg = 0; cg < CG; ++cg)
+            O[cg][jd + jj] = mfma32<kBF>(Pl[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
+      }
     // V reads (two per operand) run two operands ahead of the products that use them
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll

@@ -96,9 +96,49 @@ def test_null_pointers():
 
 
 def test_misaligned_pointer():
-    ptrs = list(FAKE)
-    ptrs[1] = ctypes.c_void_p(0x10008)
-    assert decode(dims(), ptrs) == -4
+    # out, q, k_cache, v_cache: 16 bytes; block_tables, context_lens: 4 bytes
+    for i in range(4):
+        ptrs = list(FAKE)
+        ptrs[i] = ctypes.c_void_p(0x10008)
+        assert decode(dims(), ptrs) == -4
+    for i in (4, 5):
+        ptrs = list(FAKE)
+        ptrs[i] = ctypes.c_void_p(0x10002)
+        assert decode(dims(), ptrs) == -4
+
+
+# Strides (elements; dims(): S=2, Hq=32, Hkv=4, D=128, MB=8, bf16).  pa_choose_path
+# validates the dims like every decode entry point and makes no HIP call.
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_stride_dim=2), B.PA_ERR_STRIDE),                 # innermost stride must be 1
+    (dict(out_stride_dim=3), B.PA_ERR_STRIDE),
+    (dict(out_stride_head=64), B.PA_ERR_STRIDE),             # out heads overlap (D = 128)
+    (dict(out_stride_seq=31 * 128), B.PA_ERR_STRIDE),        # out sequences overlap
+    (dict(kv_stride_block=4 * 16 * 128 - 8), B.PA_ERR_STRIDE),  # shorter than a block
+    (dict(bt_stride_seq=4), B.PA_ERR_STRIDE),                # shorter than a table row
+    (dict(q_stride_head=-128), B.PA_ERR_STRIDE),
+    (dict(q_stride_head=132), -4),                          # 264-byte rows: misaligned
+    (dict(out_stride_seq=32 * 128 + 4), -4),
+    (dict(kv_stride_block=4 * 16 * 128 + 4), -4),
+    (dict(q_stride_seq=1 << 31), -6),                       # beyond the kernels' 32 bits
+])
+def test_stride_validation(kw, status):
+    assert B.lib().pa_choose_path(ctypes.byref(dims(**kw)), 0, 512) == status
+    assert B.pa_last_error()
+    assert decode(dims(**kw)) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q_stride_seq=(32 + 8) * 128, q_stride_head=128, q_stride_dim=1),  # fused QKV view
+    dict(out_stride_seq=40 * 128, out_stride_head=128),
+    dict(q_stride_head=0, q_stride_seq=0, out_stride_dim=1),   # 0 = row-major
+    dict(kv_stride_block=2 * 4 * 16 * 128),                     # K and V interleaved per block
+    dict(bt_stride_seq=100),                                    # column slice of a wider table
+    dict(q_stride_head=64, q_stride_seq=128),                   # overlapping q rows: allowed
+])
+def test_valid_strides_pass_validation(kw):
+    assert B.lib().pa_choose_path(ctypes.byref(dims(**kw)), 0, 512) in (B.PA_PATH_V1,
+                                                                       B.PA_PATH_V2)
 
 
 def test_nonfinite_scale():
