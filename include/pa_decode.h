@@ -132,6 +132,25 @@ pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const voi
                       void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory
+ * (code under stream/graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, path rule and result as pa_decode, but the V2
+ * workspace is a static device array of PA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library (one per device, held until the process ends) instead of hipMalloc'd
+ * memory: the call makes no allocating HIP or library call.  A call whose
+ * workspace (pa_workspace_bytes with max_context_len 0) exceeds that size returns
+ * PA_ERR_WORKSPACE and enqueues nothing.  Every call on a device shares that
+ * device's array: calls that overlap on one device (different streams, or host
+ * threads) race and give undefined results.  The array needs no initialisation
+ * (every value read was written earlier in the same call).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status_t pa_decode_noalloc(const pa_dims_t* dims, void* out, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, int32_t partition_size, void* stream);
+
+/*
  * pa_workspace_bytes -- bytes of device workspace a V2 call needs.
  * max_context_len <= 0 means MB*16.  Layout (all fp32, 256-byte aligned
  * sections), with Pmax = ceil(max_context_len / partition_size):

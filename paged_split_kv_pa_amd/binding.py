@@ -65,6 +65,7 @@ _DIMS = ctypes.POINTER(PaDims)
 # name -> (restype, argtypes); mirrors include/pa_decode.h
 SIGNATURES = {
     "pa_decode": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P]),
+    "pa_decode_noalloc": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P]),
     "pa_workspace_bytes": (_SZ, [_DIMS, _I64, _I32]),
     "pa_workspace_layout": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
     "pa_decode_ex": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I32, _P, _P, _SZ,
@@ -208,6 +209,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, parti
     ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
     _check(lib().pa_decode(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
                            _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      partition_size=512, stream=None):
+    """pa_decode with the library's static scratch as the V2 workspace: no allocation."""
+    d = dims_of(q, k_cache, block_tables, out, v_cache)
+    ptrs = _tensors(out, q, k_cache, v_cache, block_tables, context_lens)
+    _check(lib().pa_decode_noalloc(ctypes.byref(d), *ptrs, float(scale), int(partition_size),
+                                   _stream(stream)))
     return out
 
 

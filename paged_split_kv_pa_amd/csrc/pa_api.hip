@@ -416,6 +416,32 @@ pa_status_t owned_workspace(size_t bytes, void** out) {
   return ok();
 }
 
+// Static scratch of pa_decode_noalloc: the V2 workspace of callers that cannot allocate.
+// Each device holds its own copy of the array for the life of the process.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device address comes
+// from hipGetSymbolAddress, once per device (with that device current), and only that
+// address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pa_status_t scratch_address(void** out) {
+  int dev = 0;
+  pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_INTERNAL, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != PA_OK) return st;
+    if (!p) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 int32_t choose(const Plan& pl, int32_t partition_size) {
   const int64_t t = v1_threshold().load();
   if (t >= 0) return pl.ctx_bound <= t ? PA_PATH_V1 : PA_PATH_V2;
@@ -424,10 +450,13 @@ int32_t choose(const Plan& pl, int32_t partition_size) {
   return (one_partition || v1_fills) ? PA_PATH_V1 : PA_PATH_V2;
 }
 
+// Where the V2 workspace of a decode call comes from.
+enum class Ws { kCaller, kOwned, kStatic };
+
 pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const void* k,
                         const void* v, const int32_t* bt, const int32_t* ctx, float scale,
                         int32_t partition_size, void* stream, void* workspace,
-                        size_t workspace_bytes, bool owned, int64_t max_context_len,
+                        size_t workspace_bytes, Ws wsm, int64_t max_context_len,
                         int32_t path, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   if (path != PA_PATH_AUTO && path != PA_PATH_V1 && path != PA_PATH_V2)
     return fail(PA_ERR_SHAPE, "path %d is not PA_PATH_AUTO, PA_PATH_V1 or PA_PATH_V2", path);
@@ -439,13 +468,22 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   if ((st = check_scale(scale)) != PA_OK) return st;
   const int32_t take = path == PA_PATH_AUTO ? choose(pl, partition_size) : path;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (wsm == Ws::kStatic) {
+    if ((st = scratch_address(&workspace)) != PA_OK) return st;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+    if (take == PA_PATH_V2 && pl.ws_bytes > workspace_bytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "this call needs %zu bytes of workspace; the static scratch of "
+                  "pa_decode_noalloc holds %zu (use pa_decode_ex with a caller workspace)",
+                  pl.ws_bytes, workspace_bytes);
+  }
   if (take == PA_PATH_V1) {
     Plan p1;
     if ((st = make_plan(dims, max_context_len, 0, false, &p1)) != PA_OK) return st;
     return run_partition(dims, p1, out, q, k, v, bt, ctx, scale, nullptr, hs, pa::Split(), e0,
                          e1);
   }
-  if (owned) {
+  if (wsm == Ws::kOwned) {
     if ((st = owned_workspace(pl.ws_bytes, &workspace)) != PA_OK) return st;
   } else {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; V2 needs %zu bytes",
@@ -541,7 +579,19 @@ pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const voi
                       void* stream) {
   try {
     return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                       partition_size, stream, nullptr, 0, true, 0, PA_PATH_AUTO);
+                       partition_size, stream, nullptr, 0, Ws::kOwned, 0, PA_PATH_AUTO);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_decode_noalloc(const pa_dims_t* dims, void* out, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, int32_t partition_size, void* stream) {
+  try {
+    return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                       partition_size, stream, nullptr, 0, Ws::kStatic, 0, PA_PATH_AUTO);
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }
@@ -580,7 +630,7 @@ pa_status_t pa_decode_ex(const pa_dims_t* dims, void* out, const void* q, const 
                          int64_t max_context_len, int32_t path) {
   try {
     return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                       partition_size, stream, workspace, workspace_bytes, false,
+                       partition_size, stream, workspace, workspace_bytes, Ws::kCaller,
                        max_context_len, path);
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
@@ -595,8 +645,9 @@ pa_status_t pa_decode_profiled(const pa_dims_t* dims, void* out, const void* q,
                                void* attn_start_event, void* attn_stop_event) {
   try {
     return decode_impl(dims, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                       partition_size, stream, workspace, workspace_bytes, workspace == nullptr,
-                       max_context_len, path, static_cast<hipEvent_t>(attn_start_event),
+                       partition_size, stream, workspace, workspace_bytes,
+                       workspace == nullptr ? Ws::kOwned : Ws::kCaller, max_context_len, path,
+                       static_cast<hipEvent_t>(attn_start_event),
                        static_cast<hipEvent_t>(attn_stop_event));
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
