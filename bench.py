@@ -598,15 +598,15 @@ def bench_decode(args, cfg, P):
     bt = torch.from_numpy(w.block_tables).cuda()
     ctx = torch.from_numpy(w.context_lens).cuda()
     out = torch.empty_like(q)
-    ws = torch.zeros(B.pa_workspace_bytes(q, kc0, bt, 0, P), dtype=torch.uint8, device="cuda")
     dims = B.dims_of(q, kc0, bt, out, vc0)
     path = {"auto": B.pa_choose_path(dims, 0, P), "v1": B.PA_PATH_V1,
             "v2": B.PA_PATH_V2}[args.path]
     stream = torch.cuda.current_stream()
 
     # Argument tuples are marshalled once, so a step costs one plain C call on the host:
-    # pa_decode_profiled = pa_decode_ex (same kernels, same workspace, same path) plus
-    # optional start/stop timestamps of the attention kernel taken by the runtime.
+    # pa_decode_profiled with no caller workspace = pa_decode (the library's workspace, the
+    # same path and kernels: V2 as a single launch where it applies) plus optional
+    # start/stop timestamps of the attention kernel taken by the runtime.
     lib = B.lib()
     dref = ctypes.byref(dims)
     vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
@@ -615,7 +615,7 @@ def bench_decode(args, cfg, P):
     def args_for(st):
         sp = ctypes.c_void_p(st.cuda_stream)
         return [[dref, vp(out), vp(q), vp(ks[c]), vp(vs[c]), vp(bt), vp(ctx), scale, P, sp,
-                 vp(ws), ws.numel(), 0, path, None, None] for c in range(R)]
+                 None, 0, 0, path, None, None] for c in range(R)]
     call_args = args_for(stream)
 
     hip = ctypes.CDLL("libamdhip64.so.7")
@@ -727,8 +727,10 @@ def bench_decode(args, cfg, P):
         (f"; graph replay {graph['us_per_step']:.2f} us/step" if graph else ""))
 
     mfma = w.dtype != "f32" and w.num_q_heads // w.num_kv_heads >= 4
+    single = path == B.PA_PATH_V2 and B.pa_fused_applies(q, kc0, bt, P)
     kernel_name = ("attn_mfma_kernel" if mfma else "attn_valu_kernel") + \
-        (" (V1 single pass)" if path == B.PA_PATH_V1 else " (V2 phase 1)")
+        (" (V1 single pass)" if path == B.PA_PATH_V1 else
+         " (V2 phase 1 and merge, one launch)" if single else " (V2 phase 1)")
     value = kvb / (ms_per_step / 1e3) / 1e9
     achieved = kvb / (k1_mean / 1e6) / 1e9
     rec = {
@@ -755,6 +757,7 @@ def bench_decode(args, cfg, P):
             "kv_bytes_per_step": kvb, "kv_pool_copies": R,
             "mfma_variant": B.pa_get_mfma_variant(),
             "work_split": list(B.pa_get_work_split()),
+            "single_launch": bool(single),
         },
         "step_us_gpu": stats(periods),
         "roofline": {

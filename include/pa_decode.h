@@ -124,6 +124,11 @@ typedef struct pa_dims {
  * workspace that grows on demand (hipMalloc on the first call that needs
  * more) and is kept per device; calls that overlap on one device from
  * different streams must use pa_decode_ex with their own workspaces.
+ * With the library's workspace, V2 can run as ONE launch (see pa_set_fused): the
+ * phase-1 work-groups publish their partials and the merge work-groups of the same
+ * grid fold them once every partition of their (sequence, KV head) is in.  The
+ * result equals the two-launch V2 to rounding (same partials, the same log-sum-exp
+ * merge, a different summation tree).
  * Returns PA_OK or an error status; on error nothing was enqueued.
  */
 pa_status_t pa_decode(const pa_dims_t* dims, void* out, const void* q, const void* k_cache,
@@ -281,6 +286,24 @@ void pa_release(void);
 
 /* Library version string, e.g. "pa_decode 0.1.0 gfx950". */
 const char* pa_version(void);
+
+/* Single-launch V2 of pa_decode, pa_decode_noalloc and pa_decode_profiled with
+ * the library's workspace.  mode 0 (default): two launches.  mode 1: one launch
+ * whenever the shape allows it (S*Hkv <= 256; S*Hq*8 merge work-groups no more than
+ * the phase-1 work-groups and at most 4096; at most 4096 partial states per head;
+ * workspace below 2 GiB), two launches otherwise.  On MI355X one launch measured
+ * slower on a 100K-token context and equal on a mixed batch, hence the default.
+ * pa_decode_ex (caller workspace) and the phase entry points always use two
+ * launches.  Env PA_FUSED sets the initial value.  Process-wide.  Returns
+ * PA_ERR_UNSUPPORTED for another mode. */
+pa_status_t pa_set_fused(int32_t mode);
+int32_t pa_get_fused(void);
+/* 1 if V2 on the library's workspace (pa_decode, pa_decode_noalloc, or
+ * pa_decode_profiled with no workspace, whenever they take V2) runs as one launch
+ * for these dims and partition size under the current settings, 0 if it takes two
+ * launches, or a negative pa_status_t.  Reads the device's compute-unit count
+ * (PA_ERR_HIP without a device). */
+int32_t pa_fused_applies(const pa_dims_t* dims, int32_t partition_size);
 
 /* Tuning knob for the fp16/bf16 kernel with G >= 4: work-group shape
  *   0 = 2 waves per (partition, KV head, sequence), 3-deep (D=128) / 2-deep

@@ -85,6 +85,9 @@ SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_set_mfma_variant": (_I32, [_I32]),
     "pa_get_mfma_variant": (_I32, []),
+    "pa_set_fused": (_I32, [_I32]),
+    "pa_get_fused": (_I32, []),
+    "pa_fused_applies": (_I32, [_DIMS, _I32]),
     "pa_set_work_split": (_I32, [_I32, _I64]),
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
     "pa_split_plan": (_I32, [_DIMS, _I64, _I32, ctypes.POINTER(_I64)]),
@@ -332,6 +335,25 @@ def pa_set_mfma_variant(variant):
 
 def pa_get_mfma_variant():
     return int(lib().pa_get_mfma_variant())
+
+
+def pa_set_fused(mode):
+    """Single-launch V2 for library-managed workspaces: 1 where it applies, 0 never
+    (the default)."""
+    _check(lib().pa_set_fused(int(mode)))
+
+
+def pa_get_fused():
+    return int(lib().pa_get_fused())
+
+
+def pa_fused_applies(q, k_cache, block_tables, partition_size=512):
+    """True if pa_decode would run V2 as a single launch for these shapes."""
+    d = dims_of(q, k_cache, block_tables)
+    r = lib().pa_fused_applies(ctypes.byref(d), int(partition_size))
+    if r < 0:
+        raise PaError(r, pa_last_error())
+    return bool(r)
 
 
 def pa_set_work_split(pieces, first_item=0):

@@ -216,6 +216,25 @@ pa_status_t make_plan(const pa_dims_t* d, int64_t max_context_len, int32_t parti
   return ok();
 }
 
+// ---- single-launch V2 (see fused_merge in pa_kernels.hip) --------------------------------
+// Setting: 0 (default) two launches; 1 one launch wherever it applies.  Measured on
+// MI355X the single launch is slower at 100K tokens (41.8 vs 38.8 us/step: its merge
+// waits on a chain of device-scope round trips after the last partition, where the second
+// launch reads partials the kernel boundary has already written back) and equal on the
+// mixed batch, so it is not the default.  Env PA_FUSED sets the initial value.
+std::atomic<int> g_fused{-2};  // -2: not yet read from the environment
+
+int fused_setting() {
+  int v = g_fused.load(std::memory_order_relaxed);
+  if (v == -2) {
+    v = 0;
+    const char* e = std::getenv("PA_FUSED");
+    if (e && (e[0] == '0' || e[0] == '1') && e[1] == '\0') v = e[0] - '0';
+    g_fused.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 // ---- work split (see pa::Split) --------------------------------------------------------
 // Setting: pieces -1 = automatic, 0 = off, 2..16 = cut every item from first_item on.
 std::atomic<int32_t> g_split_pieces{-1};
@@ -393,7 +412,12 @@ std::mutex g_ws_mutex;
 void* g_ws_ptr[kMaxDevices] = {};
 size_t g_ws_size[kMaxDevices] = {};
 
-pa_status_t owned_workspace(size_t bytes, void** out) {
+// Library-managed workspaces (pa_decode's and pa_decode_noalloc's) start with the
+// counters of a single-launch V2 (pa::kFusedCounterBytes, zero between launches); the
+// partials follow.  The counters are zeroed (by a fill kernel on the caller's stream)
+// whenever the memory is new.
+pa_status_t owned_workspace(size_t bytes, hipStream_t stream, void** out) {
+  bytes += pa::kFusedCounterBytes;
   int dev = 0;
   pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
   if (st != PA_OK) return st;
@@ -409,6 +433,13 @@ pa_status_t owned_workspace(size_t bytes, void** out) {
     void* p = nullptr;
     st = hip_status(hipMalloc(&p, bytes), "hipMalloc(workspace)");
     if (st != PA_OK) return st;
+    st = hip_status(pa::launch_zero_words(static_cast<uint32_t*>(p),
+                                          pa::kFusedCounterBytes / 4, stream),
+                    "workspace counter fill");
+    if (st != PA_OK) {
+      (void)hipFree(p);
+      return st;
+    }
     g_ws_ptr[dev] = p;
     g_ws_size[dev] = bytes;
   }
@@ -425,7 +456,9 @@ static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES]
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-pa_status_t scratch_address(void** out) {
+// The scratch's device address on the current device; on the first call per device the
+// counter region at its start is zeroed by a fill kernel on `stream`.
+pa_status_t scratch_address(hipStream_t stream, void** out) {
   int dev = 0;
   pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
   if (st != PA_OK) return st;
@@ -436,6 +469,10 @@ pa_status_t scratch_address(void** out) {
     st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
     if (st != PA_OK) return st;
     if (!p) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    st = hip_status(pa::launch_zero_words(static_cast<uint32_t*>(p),
+                                          pa::kFusedCounterBytes / 4, stream),
+                    "scratch counter fill");
+    if (st != PA_OK) return st;
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -448,6 +485,22 @@ int32_t choose(const Plan& pl, int32_t partition_size) {
   const bool one_partition = partition_size > 0 && pl.ctx_bound <= partition_size;
   const bool v1_fills = (int64_t)pl.S * pl.Hkv >= kV1FillWorkgroups;
   return (one_partition || v1_fills) ? PA_PATH_V1 : PA_PATH_V2;
+}
+
+// Whether a V2 call with this plan and split runs as a single launch (given a
+// library-managed workspace): the setting asks for it, the counters cover every (sequence,
+// KV head), the merge work-groups fit in the second grid row, the merge's LDS holds every
+// partial state of a head, and workspace offsets fit 31 bits.
+bool fused_applies(const Plan& pl, const pa::Split& sp) {
+  if (fused_setting() != 1) return false;
+  pa::AttnArgs a;
+  a.Pmax = (int32_t)pl.Pmax;
+  a.Hkv = pl.Hkv;
+  a.split = sp;
+  const long long n1 = pa::phase1_workgroups(a, pl.S);
+  const long long m = (long long)pl.S * pl.Hq * pa::kFusedChunks;
+  return (long long)pl.S * pl.Hkv <= pa::kFusedMaxGroups && m <= n1 && m <= pa::kFusedMaxMerge &&
+         pa::fold_states(a, pl.S) <= pa::kFusedMaxFold && pl.ws_bytes < (size_t(1) << 31);
 }
 
 // Where the V2 workspace of a decode call comes from.
@@ -468,14 +521,19 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   if ((st = check_scale(scale)) != PA_OK) return st;
   const int32_t take = path == PA_PATH_AUTO ? choose(pl, partition_size) : path;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint32_t* counters = nullptr;  // library-managed workspaces: the counter region
   if (wsm == Ws::kStatic) {
-    if ((st = scratch_address(&workspace)) != PA_OK) return st;
-    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
-    if (take == PA_PATH_V2 && pl.ws_bytes > workspace_bytes)
+    void* base = nullptr;
+    if ((st = scratch_address(hs, &base)) != PA_OK) return st;
+    const size_t room = PA_NOALLOC_SCRATCH_BYTES - pa::kFusedCounterBytes;
+    if (take == PA_PATH_V2 && pl.ws_bytes > room)
       return fail(PA_ERR_WORKSPACE,
                   "this call needs %zu bytes of workspace; the static scratch of "
                   "pa_decode_noalloc holds %zu (use pa_decode_ex with a caller workspace)",
-                  pl.ws_bytes, workspace_bytes);
+                  pl.ws_bytes, room);
+    counters = static_cast<uint32_t*>(base);
+    workspace = static_cast<char*>(base) + pa::kFusedCounterBytes;
+    workspace_bytes = room;
   }
   if (take == PA_PATH_V1) {
     Plan p1;
@@ -484,8 +542,11 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
                          e1);
   }
   if (wsm == Ws::kOwned) {
-    if ((st = owned_workspace(pl.ws_bytes, &workspace)) != PA_OK) return st;
-  } else {
+    void* base = nullptr;
+    if ((st = owned_workspace(pl.ws_bytes, hs, &base)) != PA_OK) return st;
+    counters = static_cast<uint32_t*>(base);
+    workspace = static_cast<char*>(base) + pa::kFusedCounterBytes;
+  } else if (wsm == Ws::kCaller) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; V2 needs %zu bytes",
                                 pl.ws_bytes);
     if (workspace_bytes < pl.ws_bytes)
@@ -495,6 +556,16 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   }
   pa::Split sp;
   if ((st = plan_split(pl, &sp)) != PA_OK) return st;
+  if (counters && fused_applies(pl, sp)) {
+    // Single launch: phase 1 and the merge in one grid (library-managed workspace only:
+    // its counter region is zero between launches).
+    pa::AttnArgs a = attn_args(pl, out, q, k, v, bt, ctx, scale, workspace, sp);
+    a.fused = 1;
+    a.fused_m = (int32_t)((long long)pl.S * pl.Hq * pa::kFusedChunks);
+    a.counters = counters;
+    return hip_status(pa::launch_attention(dims->dtype, pl.D, pl.G, a, pl.S, hs, e0, e1),
+                      "single-launch decode");
+  }
   if ((st = run_partition(dims, pl, out, q, k, v, bt, ctx, scale, workspace, hs, sp, e0, e1)) !=
       PA_OK)
     return st;
@@ -821,6 +892,24 @@ pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const 
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }
 }
+
+int32_t pa_fused_applies(const pa_dims_t* dims, int32_t partition_size) {
+  Plan pl;
+  pa_status_t st = make_plan(dims, 0, partition_size, true, &pl);
+  if (st != PA_OK) return st;
+  pa::Split sp;
+  if ((st = plan_split(pl, &sp)) != PA_OK) return st;
+  return fused_applies(pl, sp) ? 1 : 0;
+}
+
+pa_status_t pa_set_fused(int32_t mode) {
+  if (mode < 0 || mode > 1)
+    return fail(PA_ERR_UNSUPPORTED, "single-launch mode %d unknown (0 or 1)", mode);
+  g_fused.store(mode, std::memory_order_relaxed);
+  return ok();
+}
+
+int32_t pa_get_fused(void) { return fused_setting(); }
 
 pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item) {
   if (pieces != -1 && pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4 && pieces != 8 &&

@@ -56,7 +56,27 @@ struct AttnArgs {
   // work-group j takes the j-th non-empty (sequence, KV head, partition) item (see
   // compact_item).
   int32_t order_seqs = 0;
+  // Single-launch V2 (see fused_merge): grid (n1, 2); row 0 runs the phase-1 items on
+  // a linear index, row 1 the merge work-groups, fused_m of them (one per sequence,
+  // query head and kFusedChunks-th of the head dim).  counters: the arrival counter of
+  // each (sequence, KV head), then the go flag of each merge work-group (see arrive);
+  // all zero before the launch and zero again after it.
+  int32_t fused = 0;
+  int32_t fused_m = 0;
+  uint32_t* counters = nullptr;
 };
+constexpr int kFusedChunks = 8;              // merge work-groups per query head
+// Arrival counter of (sequence, KV head) i at word kFusedCounterStride * i; go flag of
+// merge work-group m at word kFusedFlagBase + kFusedFlagStride * m.  Every counter and
+// flag has a line of its own.
+constexpr int kFusedCounterStride = 64;      // uint32 words (256 bytes)
+constexpr int kFusedMaxGroups = 256;         // (sequence, KV head) pairs
+constexpr int kFusedFlagBase = kFusedCounterStride * kFusedMaxGroups;
+constexpr int kFusedFlagStride = 16;         // uint32 words (64 bytes)
+constexpr int kFusedMaxMerge = 4096;         // merge work-groups
+constexpr size_t kFusedCounterBytes =
+    4 * ((size_t)kFusedFlagBase + (size_t)kFusedFlagStride * kFusedMaxMerge);  // 320 KiB
+constexpr int kFusedMaxFold = 4096;          // partial states per head a merge holds in LDS
 constexpr int kOrderMaxSeqs = 512;  // longest-first orders (V1, prefill): at most this many sequences
 
 // Arguments of the phase-2 (cross-partition) kernel.
@@ -86,6 +106,13 @@ Kernel kernel_for(int dtype, int group);
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
                             hipStream_t stream, hipEvent_t ev_start = nullptr,
                             hipEvent_t ev_stop = nullptr);
+// Zero n uint32 words at p (a fill kernel: graph-capture safe, unlike hipMemsetAsync).
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);
+// Work-groups phase 1 of V2 runs for this launch (grid slots of the item order, or the
+// work split's linear grid).
+long long phase1_workgroups(const AttnArgs& a, int num_seqs);
+// Partial states (partitions plus pieces of cut ones) phase 2 folds per head, at most.
+long long fold_states(const AttnArgs& a, int num_seqs);
 // Launch the phase-2 kernel on grid (S*Hq, 8), or (S*Hq, 1) for many heads.
 hipError_t launch_reduce(int dtype, int head_dim, const ReduceArgs& a, int num_seqs,
                          hipStream_t stream);

@@ -205,8 +205,8 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // a load of its argument block.  A by-value struct argument is never preloaded.
 // The hardware preloads at most 14 argument dwords (16 user registers, two of which hold
 // the argument-block address): three pointers and eight integers, two of them packed
-// (the number of KV heads with the sequence-order count, the split's first cut item with
-// its piece shift).
+// (the number of KV heads with the sequence-order count; the split's first cut item with
+// its piece shift and, in bit 30, the single-launch flag).
 #define PA_ATTN_LEAD_PARAMS                                                                \
   const int32_t *lead_ctx, const int32_t *lead_bt, const void *lead_q, int32_t lead_Pmax, \
       int32_t lead_hkv_order, int32_t lead_MB, int32_t lead_P, int32_t lead_q_sh,         \
@@ -227,7 +227,8 @@ __device__ __forceinline__ AttnArgs with_lead(AttnArgs a, const int32_t* ctx, co
   a.P = P;
   a.q_sh = q_sh;
   a.split.shift = first_shift & 15;
-  a.split.first = first_shift >> 4;
+  a.split.first = (first_shift >> 4) & 0x3ffffff;
+  a.fused = (first_shift >> 30) & 1;
   a.q_ss = q_ss;
   a.bt_ss = bt_ss;
   return a;
@@ -255,14 +256,15 @@ struct Item {
 __device__ __forceinline__ Item grid_item(const AttnArgs& a) {
   Item it;
   it.piece = -1;
-  if (a.split.shift == 0) {
+  if (a.split.shift == 0 && !a.fused) {
     it.p = blockIdx.x;
     it.g = blockIdx.y;
     it.b = blockIdx.z;
     return it;
   }
+  // linear grid: the work split, or a single-launch V2 (row 0 of its grid)
   int j = blockIdx.x;
-  if (j >= a.split.first) {
+  if (a.split.shift > 0 && j >= a.split.first) {
     const int t = j - a.split.first;
     j = a.split.first + (t >> a.split.shift);
     it.piece = t & ((1 << a.split.shift) - 1);
@@ -322,7 +324,8 @@ __device__ __forceinline__ Part plan_partition(const AttnArgs& a, const Item& it
 // counts of sequences 8l .. 8l+7 (S <= 512), a wave scan gives each lane's first item,
 // and the lane whose range holds j finds the sequence.
 __device__ __forceinline__ bool compact_item(const AttnArgs& a, int S, Item& it) {
-  const int j = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int j = a.fused ? (int)blockIdx.x
+                        : (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
   const int lane = threadIdx.x & 63;
   const int cap = a.MB * kBlockSize;
   int np[8];
@@ -424,6 +427,66 @@ __device__ __forceinline__ void partial_rows(const AttnArgs& a, const Item& it, 
   }
 }
 
+// ---- single-launch V2: publication of the phase-1 partials ----------------------------
+// In a single-launch V2 the merge work-groups of the same grid read the partials, so they
+// are stored with device-scope (sc1) stores -- coherent across the XCDs' L2 caches once
+// complete -- and each phase-1 work-group then counts itself in its (sequence, KV head)
+// arrival counter (see fused_merge).
+constexpr int kScDevice = 16;  // cache-policy bits of a device-scope access (sc1)
+
+// Stores 8 (or 4, 2) fp32 values at dst inside the workspace that starts at ws, with
+// device-scope stores.  The buffer resource spans the whole workspace (the host keeps
+// fused workspaces below 4 GiB), so it is the same in every lane.
+template <int N>
+__device__ __forceinline__ void store_f32_dev(const float* ws, float* dst, const float* v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ws), (short)0, -1, 0x00020000);
+  const int off = (int)((const char*)dst - (const char*)ws);
+  if constexpr (N == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])}, r,
+                                          off, 0, kScDevice);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(v[i]), __float_as_uint(v[i + 1]), __float_as_uint(v[i + 2]),
+                __float_as_uint(v[i + 3])},
+          r, off + 4 * i, 0, kScDevice);
+  }
+}
+__device__ __forceinline__ void store_stat_dev(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ int fused_expected(const AttnArgs& a, int b, int g, int n);
+
+// Called by every phase-1 work-group of a single-launch V2 exactly once, from wave 0,
+// after its last partial store was issued: waits until this wave's stores are complete,
+// then counts the work-group in the (sequence, KV head) arrival counter.  The work-group
+// that completes the count (every other one has counted itself, so every partial of the
+// group is visible) resets the counter for the next launch and raises the go flag of
+// each of the group's G * kFusedChunks merge work-groups, one per lane.  Only the flag
+// owners poll them, each its own line: polls never queue the arrivals.
+// n: the sequence's context length as read from context_lens.
+template <int G>
+__device__ __forceinline__ void arrive(const AttnArgs& a, int b, int g, int n) {
+  if (!a.fused) return;
+  __builtin_amdgcn_s_waitcnt(0);  // every store of this wave performed
+  const int lane = threadIdx.x & 63;
+  uint32_t* const cnt = a.counters + kFusedCounterStride * ((size_t)b * a.Hkv + g);
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  const int cap = a.MB * kBlockSize;
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  if (prev + 1 != (unsigned)fused_expected(a, b, g, n)) return;
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int m0 = ((b * a.Hq) + g * G) * kFusedChunks;
+#pragma unroll
+  for (int k = lane; k < G * kFusedChunks; k += 64)
+    __hip_atomic_store(a.counters + kFusedFlagBase + kFusedFlagStride * (m0 + k), 1u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Element offsets of row (sequence b, query head h) of q and of out.
 __device__ __forceinline__ size_t q_offset(const AttnArgs& a, int b, int h) {
   return (size_t)b * (uint32_t)a.q_ss + (size_t)h * (uint32_t)a.q_sh;
@@ -439,6 +502,214 @@ __device__ __forceinline__ void write_zero_group(const AttnArgs& a, int b, int g
   for (int idx = threadIdx.x * 4; idx < G * D; idx += blockDim.x * 4) {
     const int h = idx / D, d = idx - h * D;
     store_out<DT, 4>(a.out, out_offset(a, b, g * G + h) + d, z);
+  }
+}
+
+// =======================================================================================
+// Single-launch V2: the merge work-groups ("Phase 2: Cross-partition reduction
+// (log-sum-exp)", project_6 commit 96f4baf page, V2 plan, in the same launch as phase 1).
+//
+// Row 1 of the grid: work-group m takes sequence b, query head hq and the kFusedChunks-th
+// part `chunk` of the head dim (m = (b Hq + hq) kFusedChunks + chunk).  It waits for its
+// go flag, which the phase-1 work-group that completes the count of (b, KV head hq / G)
+// raises (see arrive): the phase-1 work-groups have lower grid indices and are dispatched
+// first, so they are resident or finished while it waits.  It clears the flag for the
+// next launch, folds the partial states like reduce_kernel, with device-scope loads, and
+// writes its columns of out.  The wait is bounded by a wall-clock limit: a protocol error
+// would show as NaN outputs (and a flag raised after the limit would stay raised), never
+// as a hang.
+// =======================================================================================
+constexpr uint64_t kFusedWaitTicks = 1ull << 25;  // s_memrealtime runs at 100 MHz: ~0.34 s
+
+
+__device__ int fused_expected(const AttnArgs& a, int b, int g, int n) {
+  if (a.order_seqs > 0 && a.Pmax > 1) {  // compacted order: the real items only
+    int c = (n + a.P - 1) / a.P;
+    return c > a.Pmax ? a.Pmax : (c < 1 ? 1 : c);
+  }
+  if (a.split.shift == 0) return a.Pmax;  // every grid slot of (b, g)
+  const long long j0 = (long long)a.Pmax * ((long long)g + (long long)a.Hkv * b);
+  long long cut = j0 + a.Pmax - (a.split.first > j0 ? (long long)a.split.first : j0);
+  cut = cut < 0 ? 0 : cut;
+  return (int)((a.Pmax - cut) + (cut << a.split.shift));
+}
+
+template <int DT, int D, int T>
+__device__ __forceinline__ void fused_merge(const AttnArgs& a) {
+  constexpr int kCols = D / kFusedChunks;
+  constexpr int NC4 = kCols / 4;   // float4 column lanes
+  constexpr int NPG = T / NC4;     // partial-state lanes
+  constexpr int NWV = T / 64;
+  static_assert(NC4 >= 1 && NC4 <= 64 && T % NC4 == 0, "");
+  extern __shared__ float s_w[];   // one weight per partial state (sized at launch)
+  __shared__ float s_red[NWV];
+  __shared__ f32x4 s_acc[NWV][NC4];
+  __shared__ int s_ok;
+  const int m = blockIdx.x;
+  if (m >= a.fused_m) return;
+  const int chunk = m % kFusedChunks;
+  const int bh = m / kFusedChunks;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const int g = hq / G, gq = hq - g * G;
+  const int tid = threadIdx.x;
+  const int d4 = tid % NC4, pg = tid / NC4;
+  const int lane = tid & 63, wv = tid >> 6;
+
+  int n = a.ctx[b];
+  const int cap = a.MB * kBlockSize;
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  int nparts = (n + a.P - 1) / a.P;
+  if (nparts > a.Pmax) nparts = a.Pmax;
+  // Partial states to fold, as in reduce_kernel: partitions [0, p_split) from their rows,
+  // then each cut partition's non-empty pieces from consecutive piece slots.
+  const int sh = a.split.shift;
+  int p_split = nparts, nfold = nparts, slot0 = 0;
+  if (sh > 0) {
+    const long long item0 = (long long)a.Pmax * ((long long)g + (long long)a.Hkv * b);
+    const long long first = (long long)a.split.first - item0;
+    const int nom_split = first <= 0 ? 0 : (first >= a.Pmax ? a.Pmax : (int)first);
+    if (nom_split < a.Pmax) slot0 = (int)((item0 + nom_split - a.split.first) << sh);
+    p_split = nom_split < nparts ? nom_split : nparts;
+    if (p_split < nparts) {
+      const int sub = a.P >> sh;
+      const int last_tok = min(a.P, n - (nparts - 1) * a.P);
+      nfold = p_split + ((nparts - 1 - p_split) << sh) + (last_tok + sub - 1) / sub;
+    }
+  }
+  const bool merge = !(p_split == nparts && nparts <= 1);  // else phase 1 wrote out
+
+  uint32_t* const flag = a.counters + kFusedFlagBase + kFusedFlagStride * (size_t)m;
+  if (tid == 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    int ok = 1;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kFusedWaitTicks) {
+        ok = 0;
+        break;
+      }
+    }
+    if (ok) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = ok;
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0;
+  const int col = chunk * kCols + d4 * 4;
+  const size_t orow = (size_t)b * (size_t)a.o_ss + (size_t)hq * (size_t)a.o_sh;
+  if (!ok) {  // the wait ran out: make it visible in the output
+    if (tid < NC4) {
+      const float nan = __builtin_nanf("");
+      const float vals[4] = {nan, nan, nan, nan};
+      store_out<DT, 4>(a.out, orow + col, vals);
+    }
+    return;
+  }
+  if (merge) {
+    // Byte offsets from the workspace base (tmp_out) of a state's row and statistics.
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(a.tmp_out, (short)0, -1, 0x00020000);
+    const long long base = (long long)bh * a.Pmax;
+    const char* const wsb = (const char*)a.tmp_out;
+    const long long o_max = (const char*)a.max_logits - wsb, o_sum = (const char*)a.exp_sums - wsb;
+    const long long o_pout = sh ? (const char*)a.split.piece_out - wsb : 0;
+    const long long o_pmax = sh ? (const char*)a.split.piece_max - wsb : 0;
+    const long long o_psum = sh ? (const char*)a.split.piece_sum - wsb : 0;
+    auto prow = [&](int q) { return (long long)(slot0 + q - p_split) * G + gq; };
+    auto off_o = [&](int q) -> int {
+      return (int)(q < p_split ? ((base + q) * D + col) * 4 : o_pout + (prow(q) * D + col) * 4);
+    };
+    auto load_ms = [&](int q, float& mv, float& sv) {
+      const bool whole = q < p_split;
+      const int om = (int)(whole ? o_max + (base + q) * 4 : o_pmax + prow(q) * 4);
+      const int os = (int)(whole ? o_sum + (base + q) * 4 : o_psum + prow(q) * 4);
+      mv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, om, 0, kScDevice));
+      sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, os, 0, kScDevice));
+    };
+    // Every load of the first kMS statistics and kMO rows per lane is issued before any is
+    // used (indices past the list re-read its last entry), so the fold costs one memory
+    // round trip; longer lists finish in loops.
+    constexpr int kMS = 8, kMO = 24;
+    float sm[kMS], ss[kMS];
+    f32x4 so[kMO];
+#pragma unroll
+    for (int j = 0; j < kMS; ++j) load_ms(min(tid + T * j, nfold - 1), sm[j], ss[j]);
+#pragma unroll
+    for (int i = 0; i < kMO; ++i)
+      so[i] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off_o(min(pg + NPG * i, nfold - 1)), 0,
+                                                       kScDevice));
+    // Maxima (base 2) into LDS and their block max.
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kMS; ++j) {
+      const int q = tid + T * j;
+      if (q < nfold) {
+        const float m2 = sm[j] * kLog2e;
+        s_w[q] = m2;
+        s_w[nfold + q] = ss[j];
+        mx = fmaxf(mx, m2);
+      }
+    }
+    for (int q = tid + T * kMS; q < nfold; q += T) {
+      float mv, sv;
+      load_ms(q, mv, sv);
+      const float m2 = mv * kLog2e;
+      s_w[q] = m2;
+      s_w[nfold + q] = sv;
+      mx = fmaxf(mx, m2);
+    }
+    mx = lane_reduce<false, 1>(mx);
+    if (lane == 0) s_red[wv] = mx;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
+    // Weights r_q = exp2(m_q - M) s_q and their sum (each lane its own statistics).
+    float wsum = 0.f;
+    for (int q = tid; q < nfold; q += T) {
+      const float rq = exp2_fast(s_w[q] - M) * s_w[nfold + q];
+      s_w[q] = rq;
+      wsum += rq;
+    }
+    wsum = lane_reduce<true, 1>(wsum);
+    __syncthreads();  // weights visible; s_red reads of M done
+    if (lane == 0) s_red[wv] = wsum;
+    // sum_q r_q o_q over this lane's states.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMO; ++i)
+      if (pg + NPG * i < nfold) acc += so[i] * s_w[pg + NPG * i];
+    for (int q0 = pg + NPG * kMO; q0 < nfold; q0 += 8 * NPG) {
+      f32x4 o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = min(q0 + NPG * i, nfold - 1);
+        o[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off_o(q), 0,
+                                                                               kScDevice));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (q0 + NPG * i < nfold) acc += o[i] * s_w[q0 + NPG * i];
+    }
+    if constexpr (NC4 < 64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = lane_reduce<true, NC4>(acc[j]);
+    }
+    if (lane < NC4) s_acc[wv][d4] = acc;
+    __syncthreads();
+    if (tid < NC4) {
+      float total = s_red[0];
+      f32x4 o = s_acc[0][d4];
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) {
+        total += s_red[i];
+        o += s_acc[i][d4];
+      }
+      const float inv = 1.f / total;
+      const float vals[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      store_out<DT, 4>(a.out, orow + col, vals);
+    }
   }
 }
 
@@ -487,6 +758,10 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   __shared__ __attribute__((aligned(16))) int s_len[NW == 4 ? kOrderMaxSeqs : 4];
   __shared__ int s_pick;
 
+  if (a.fused && blockIdx.y != 0) {  // single-launch V2: a merge work-group
+    fused_merge<DT, D, NW * 64>(a);
+    return;
+  }
   Item it = grid_item(a);
   if (a.order_seqs > 0) {
     if (a.Pmax > 1) {
@@ -534,9 +809,13 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
   const Part pt = plan_partition(a, it, n_ctx);
   if (it.p >= pt.nparts) {
     if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
+    if (threadIdx.x < 64) arrive<G>(a, b, g, n_ctx);
     return;
   }
-  if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
+  if (pt.ntok <= 0) {  // empty piece: phase 2 does not read its slot
+    if (threadIdx.x < 64) arrive<G>(a, b, g, n_ctx);
+    return;
+  }
   // pt.nblk <= nblk_nom: the context never extends past the table, so every block id
   // used below is among those fetched above.
   const int kcount = w < pt.nblk ? (pt.nblk - w + NW - 1) / NW : 0;
@@ -581,7 +860,8 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
         vr[c][i] = ld_stream(rv, ((4 * kg + i) * D + 128 * c + 8 * r16) * 2);
   };
 
-  auto compute_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
+  // QK^T and the online softmax of one block; returns the PV A operand.
+  auto qk_softmax = [&](u32x4 (&kr)[NKK], int kidx) -> u32x4 {
     // S^T = K Q^T: lane (r16, kg) gets tokens 4*kg + i of head r16.  The query
     // fragments are re-read from LDS every block rather than pinned in registers;
     // the opaque lane index keeps the compiler from hoisting the reads.
@@ -650,6 +930,11 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
                ((hf[2] + half_lo<DT>(l23)) + (hf[3] + half_hi<DT>(l23)));
       pa = u32x4{h01, h23, l01, l23};
     }
+    return pa;
+  };
+  // O += P V for one block (V rows past the context are zeroed first).
+  auto pv = [&](u32x4 (&vr)[NC][4], int kidx, const u32x4 pa) {
+    const int valid = pt.ntok - (w + NW * kidx) * kBlockSize;  // >= 1, wave-uniform
     if (valid < kBlockSize) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -667,6 +952,9 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
         const uint32_t v23 = __builtin_amdgcn_perm(vr[c][3][j >> 1], vr[c][2][j >> 1], sel);
         O[8 * c + j] = mfma_16x16x32<kBF>(pa, u32x4{v01, v23, v01, v23}, O[8 * c + j]);
       }
+  };
+  auto compute_block = [&](u32x4 (&kr)[NKK], u32x4 (&vr)[NC][4], int kidx) {
+    pv(vr, kidx, qk_softmax(kr, kidx));
   };
 
   // Blocks are taken 64 at a time (one block id per lane).  Inside a chunk the NBUF
@@ -769,6 +1057,8 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
       const int d0 = 128 * c + 8 * r16;
       if (single)
         store_out<DT, 8>(a.out, orow + d0, vals);
+      else if (a.fused)
+        store_f32_dev<8>(a.tmp_out, po + d0, vals);
       else
         store_f32<8>(po + d0, vals);
     }
@@ -778,9 +1068,15 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
     head_stats(r16, fac, Mt, L);
     float *po, *pm, *ps;
     partial_rows<G, D>(a, it, r16, po, pm, ps);
-    *pm = Mt * kLn2;
-    *ps = L;
+    if (a.fused) {
+      store_stat_dev(pm, Mt * kLn2);
+      store_stat_dev(ps, L);
+    } else {
+      *pm = Mt * kLn2;
+      *ps = L;
+    }
   }
+  arrive<G>(a, b, g, n_ctx);
 }
 
 // =======================================================================================
@@ -839,6 +1135,10 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
   float* s_p = reinterpret_cast<float*>(smem + kQBytes);   // [kWaves][16][G]
   float* s_o = reinterpret_cast<float*>(smem);             // [kWaves-1][G*VE][64] after it
 
+  if (a.fused && blockIdx.y != 0) {  // single-launch V2: a merge work-group
+    fused_merge<DT, D, kThreads>(a);
+    return;
+  }
   Item it = grid_item(a);
   if (a.order_seqs > 0 && a.Pmax > 1 && !compact_item(a, a.order_seqs, it)) return;
   const int g = it.g, b = it.b;
@@ -878,9 +1178,13 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
   const Part pt = plan_partition(a, it, n_ctx);
   if (it.p >= pt.nparts) {
     if (it.p == 0 && it.piece <= 0) write_zero_group<DT, D, G>(a, b, g);
+    if (threadIdx.x < 64) arrive<G>(a, b, g, n_ctx);
     return;
   }
-  if (pt.ntok <= 0) return;  // empty piece: phase 2 does not read its slot
+  if (pt.ntok <= 0) {  // empty piece: phase 2 does not read its slot
+    if (threadIdx.x < 64) arrive<G>(a, b, g, n_ctx);
+    return;
+  }
   // pt.nblk <= nblk_nom, so the first chunk's block ids are all in btv.
   const int kcount = w < pt.nblk ? (pt.nblk - w + kWaves - 1) / kWaves : 0;
   asm volatile("" : "+v"(btv));  // see attn_mfma_kernel
@@ -1061,14 +1365,23 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(PA_ATTN_LEAD_PARAMS
       float *po, *pm, *ps;
       partial_rows<G, D>(a, it, h, po, pm, ps);
       float* dst = po + lane * VE;
-      if constexpr (VE == 2) *reinterpret_cast<f32x2*>(dst) = f32x2{vals[0], vals[1]};
-      else store_f32<VE>(dst, vals);
-      if (lane == 0) {
-        *pm = Mt * kLn2;
-        *ps = L;
+      if (a.fused) {
+        store_f32_dev<VE>(a.tmp_out, dst, vals);
+        if (lane == 0) {
+          store_stat_dev(pm, Mt * kLn2);
+          store_stat_dev(ps, L);
+        }
+      } else {
+        if constexpr (VE == 2) *reinterpret_cast<f32x2*>(dst) = f32x2{vals[0], vals[1]};
+        else store_f32<VE>(dst, vals);
+        if (lane == 0) {
+          *pm = Mt * kLn2;
+          *ps = L;
+        }
       }
     }
   }
+  arrive<G>(a, b, g, n_ctx);
 }
 
 // =======================================================================================
@@ -1315,22 +1628,25 @@ int mfma_variant(const dim3& grid, int partition_tokens, bool single_pass) {
 }
 
 struct Launch {
-  dim3 grid;
+  dim3 grid;        // the launch grid (row 1 of a single-launch V2 included)
+  dim3 work;        // the phase-1 part of it (kernel-shape choice)
+  size_t lds;       // dynamic LDS bytes (the merge weights of a single-launch V2)
   hipStream_t st;
   hipEvent_t e0, e1;
 };
 
 template <typename K>
 void launch(K kernel, const Launch& l, int threads, const AttnArgs& a) {
-  hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), 0, l.st, l.e0, l.e1, 0, a.ctx, a.bt, a.q,
-                        a.Pmax, a.Hkv | (a.order_seqs << 16), a.MB, a.P, a.q_sh,
-                        (a.split.first << 4) | a.split.shift, a.q_ss, a.bt_ss, a);
+  hipExtLaunchKernelGGL(kernel, l.grid, dim3(threads), l.lds, l.st, l.e0, l.e1, 0, a.ctx, a.bt,
+                        a.q, a.Pmax, a.Hkv | (a.order_seqs << 16), a.MB, a.P, a.q_sh,
+                        (a.split.first << 4) | a.split.shift | (a.fused ? 1 << 30 : 0), a.q_ss,
+                        a.bt_ss, a);
 }
 
 template <int DT, int D, int G>
 hipError_t launch_attn_t(const AttnArgs& a, const Launch& l) {
   if constexpr ((DT == PA_BF16 || DT == PA_F16) && G >= 4) {
-    switch (mfma_variant(l.grid, a.P, a.Pmax == 1)) {
+    switch (mfma_variant(l.work, a.P, a.Pmax == 1)) {
       case 0: launch(attn_mfma_kernel<DT, D, G, 2, (D == 128 ? 3 : 2)>, l, 2 * 64, a); break;
       case 1: launch(attn_mfma_kernel<DT, D, G, 1, 2>, l, 64, a); break;
       case 3: launch(attn_mfma_kernel<DT, D, G, 1, (D == 128 ? 5 : 3)>, l, 64, a); break;
@@ -1407,7 +1723,19 @@ hipError_t launch_reduce_d(int D, const ReduceArgs& a, int S, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 int set_mfma_variant(int v) {
   if (v < kAutoVariant || v > 3) return -1;
@@ -1421,17 +1749,42 @@ Kernel kernel_for(int dtype, int group) {
   return (dtype != PA_F32 && group >= 4) ? Kernel::kMfma : Kernel::kValu;
 }
 
+long long phase1_workgroups(const AttnArgs& a, int num_seqs) {
+  const long long items = (long long)a.Pmax * a.Hkv * num_seqs;
+  if (a.split.shift == 0) return items;
+  return a.split.first + ((items - a.split.first) << a.split.shift);
+}
+
+long long fold_states(const AttnArgs& a, int num_seqs) {
+  long long fold = a.Pmax;
+  if (a.split.shift > 0) {
+    const long long items = (long long)a.Pmax * a.Hkv * num_seqs;
+    const long long cut = (items - a.split.first) << a.split.shift;
+    fold += std::min(cut, (long long)a.Pmax << a.split.shift);
+  }
+  return fold;
+}
+
 hipError_t launch_attention(int dtype, int head_dim, int group, const AttnArgs& a, int num_seqs,
                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   dim3 grid(a.Pmax, a.Hkv, num_seqs);
+  const long long items = (long long)a.Pmax * a.Hkv * num_seqs;
+  const long long wgs = phase1_workgroups(a, num_seqs);
   if (a.split.shift > 0) {
-    const long long items = (long long)a.Pmax * a.Hkv * num_seqs;
-    const long long wgs = a.split.first + ((items - a.split.first) << a.split.shift);
     if (a.split.first < 0 || a.split.first > items || wgs > kMaxSplitGrid)
       return hipErrorInvalidValue;
     grid = dim3((unsigned)wgs, 1, 1);
   }
-  const Launch l{grid, stream, ev_start, ev_stop};
+  Launch l{grid, grid, 0, stream, ev_start, ev_stop};
+  if (a.fused) {
+    // Row 0: the phase-1 work-groups on a linear index; row 1: the merge work-groups
+    // (the first fused_m of its wgs slots).  The host checked fused_m <= wgs, the
+    // counters and the workspace size.
+    if (wgs > kMaxSplitGrid || a.fused_m > wgs || !a.counters) return hipErrorInvalidValue;
+    l.grid = dim3((unsigned)wgs, 2, 1);
+    l.work = dim3((unsigned)wgs, 1, 1);
+    l.lds = (size_t)2 * fold_states(a, num_seqs) * sizeof(float);
+  }
   // Longest-first order for V1 on the matrix-core kernel when the grid has more (sequence,
   // KV head) items than compute units, i.e. runs in more than one wave of work-groups,
   // and a work-group covers more than 1024 tokens (the four-wave shape).  The ordering

@@ -69,6 +69,18 @@ def small_workload(seed, ctx, Hq, Hkv, D, dtype, **kw):
 
 
 @contextlib.contextmanager
+def fused_mode(mode):
+    """Run the block with the library's single-launch setting changed, then restore it."""
+    from paged_split_kv_pa_amd import binding as B
+    old = B.pa_get_fused()
+    B.pa_set_fused(mode)
+    try:
+        yield
+    finally:
+        B.pa_set_fused(old)
+
+
+@contextlib.contextmanager
 def work_split(pieces, first_item=0):
     """Run the block with the library's work-split setting changed, then restore it."""
     from paged_split_kv_pa_amd import binding as B

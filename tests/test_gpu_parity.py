@@ -14,7 +14,7 @@ import oracle
 from paged_split_kv_pa_amd import binding as B
 from paged_split_kv_pa_amd import workloads as wl
 
-from helpers import check_close, small_workload, to_f64, upload, work_split
+from helpers import check_close, fused_mode, small_workload, to_f64, upload, work_split
 
 pytestmark = pytest.mark.gpu
 
@@ -347,13 +347,13 @@ def test_runs_are_bitwise_deterministic(cfg):
 
 
 def test_pa_decode_equals_its_two_phases():
-    """pa_decode (library workspace) == pa_decode_ex V2 == pa_v2_partition + pa_v2_reduce,
-    bit for bit with the work split off (the phase entry points never cut), and within
-    tolerance of the oracle."""
+    """pa_decode (library workspace, two launches) == pa_decode_ex V2 == pa_v2_partition +
+    pa_v2_reduce, bit for bit with the work split off (the phase entry points never cut),
+    and within tolerance of the oracle."""
     w, dev, ref = config_case(2)
     say("pa_decode vs pa_decode_ex vs the two phases on long_100k")
     out1 = torch.empty_like(dev["q"])
-    with work_split(0):
+    with work_split(0), fused_mode(0):
         B.pa_decode(out1, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                     dev["context_lens"], w.scale, 512)
         out0 = run_path(w, dev, B.PA_PATH_V2, 512)

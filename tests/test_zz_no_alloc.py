@@ -1,8 +1,8 @@
-"""pa_decode_noalloc (the allocation-free decode entry point) against pa_decode_ex.
+"""pa_decode_noalloc (the allocation-free decode entry point) against pa_decode.
 
 Two calls in a row through the C ABI, the second with a smaller input, each compared with
-pa_decode_ex on a caller workspace (same path rule, same kernels: bitwise equal) and with
-the float64 oracle at the fp16/bf16 tolerance.  The static scratch keeps the first call's
+pa_decode (same path rule, same kernels: bitwise equal), and, like pa_decode_ex on a
+caller workspace, with the float64 oracle at the fp16/bf16 tolerance.  The static scratch keeps the first call's
 contents, which must not leak into the second.  A call whose workspace would exceed the
 scratch is refused on the host with PA_ERR_WORKSPACE.
 """
@@ -42,13 +42,18 @@ def _run_both(w, P):
     B.pa_decode_noalloc(got, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                         dev["context_lens"], w.scale, P)
     want = torch.empty_like(dev["q"])
+    B.pa_decode(want, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                dev["context_lens"], w.scale, P)
+    two = torch.empty_like(dev["q"])
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    B.pa_decode_ex(want, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+    B.pa_decode_ex(two, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                    dev["context_lens"], w.scale, P, workspace=ws)
     torch.cuda.synchronize()
     check_close(to_f64(got), ref, "pa_decode_noalloc")
+    check_close(to_f64(two), ref, "pa_decode_ex")
+    # same path and kernels as pa_decode (single launch where it applies): same bits
     assert torch.equal(got.view(torch.int16), want.view(torch.int16)), \
-        "pa_decode_noalloc and pa_decode_ex differ"
+        "pa_decode_noalloc and pa_decode differ"
 
 
 def test_two_calls_second_smaller():
