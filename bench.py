@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 MFMA_PEAK_TFLOPS_16BIT = 2500.0  # MI355X dense bf16 / fp16 matrix-core peak
 KERNEL_SOURCE = os.path.join(ROOT, "paged_split_kv_pa_amd", "csrc", "pa_kernels.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_long_100k_hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_kernel_long_100k_p512.md")
 
 
 def counted_traffic():
@@ -201,12 +201,14 @@ def stats(xs):
             "p90": round(float(np.percentile(xs, 90)), 3), "n": int(xs.size)}
 
 
-def sweep_paths(steps=40, warmup=5):
+def sweep_paths(reps=20):
     """Forced V1 vs forced V2 step time over (batch, context); prints JSON lines.
 
-    Inputs are random bf16 tensors drawn on the device (the values do not matter for
-    timing; parity is covered by the tests).  Steps run back to back on one pool, so
-    small cases are cache-warm; both paths see the same conditions.
+    Each step is timed on the GPU side: a rotation of steps over cold copies of the KV
+    pool is captured in a graph and replayed, so the host's per-call cost does not enter
+    (the wall-clock rate of eager calls is printed beside it).  Inputs are random bf16
+    tensors drawn on the device (the values do not matter for timing; parity is covered
+    by the tests).
     """
     import torch
     from paged_split_kv_pa_amd import binding as B
@@ -219,31 +221,57 @@ def sweep_paths(steps=40, warmup=5):
                 continue
             nb = -(-n // 16)
             NB = S * nb + 1
+            pool_bytes = 2 * NB * Hkv * 16 * D * 2
+            R = max(2, -(-(1 << 30) // pool_bytes))
             q = torch.randn(S, Hq, D, device="cuda", dtype=torch.bfloat16, generator=gen)
-            k = torch.randn(NB, Hkv, 16, D, device="cuda", dtype=torch.bfloat16, generator=gen)
-            v = torch.randn_like(k)
+            ks = [torch.randn(NB, Hkv, 16, D, device="cuda", dtype=torch.bfloat16, generator=gen)
+                  for _ in range(R)]
+            vs = [torch.randn_like(k) for k in ks]
             bt = torch.randperm(NB - 1, device="cuda", generator=gen)[:S * nb].view(S, nb)
             bt = bt.to(torch.int32).contiguous()
             ctx = torch.full((S,), n, dtype=torch.int32, device="cuda")
             out = torch.empty_like(q)
-            ws = torch.empty(B.pa_workspace_bytes(q, k, bt, 0, P), dtype=torch.uint8,
+            ws = torch.empty(B.pa_workspace_bytes(q, ks[0], bt, 0, P), dtype=torch.uint8,
                              device="cuda")
             res = {}
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
             for name, path in (("v1", B.PA_PATH_V1), ("v2", B.PA_PATH_V2)):
-                for _ in range(warmup):
-                    B.pa_decode_ex(out, q, k, v, bt, ctx, 0.088, P, workspace=ws, path=path)
+                def steps(count):
+                    for i in range(count):
+                        B.pa_decode_ex(out, q, ks[i % R], vs[i % R], bt, ctx, 0.088, P,
+                                       stream=st, workspace=ws, path=path)
+                with torch.cuda.stream(st):
+                    steps(R)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    steps(R)
+                for _ in range(2):
+                    g.replay()
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
-                for _ in range(steps):
-                    B.pa_decode_ex(out, q, k, v, bt, ctx, 0.088, P, workspace=ws, path=path)
+                for _ in range(reps):
+                    g.replay()
                 torch.cuda.synchronize()
-                res[name] = (time.perf_counter() - t0) * 1e6 / steps
+                res[name] = (time.perf_counter() - t0) * 1e6 / (reps * R)
+                with torch.cuda.stream(st):
+                    steps(2)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                with torch.cuda.stream(st):
+                    steps(4 * R)
+                torch.cuda.synchronize()
+                res[name + "_eager"] = (time.perf_counter() - t0) * 1e6 / (4 * R)
+                del g
             rec = {"num_seqs": S, "context": n, "us_v1": round(res["v1"], 2),
-                   "us_v2": round(res["v2"], 2),
-                   "faster": "v1" if res["v1"] <= res["v2"] else "v2"}
+                   "us_v2": round(res["v2"], 2), "us_v1_eager": round(res["v1_eager"], 2),
+                   "us_v2_eager": round(res["v2_eager"], 2),
+                   "faster": "v1" if res["v1"] <= res["v2"] else "v2",
+                   "auto": "v1" if B.pa_choose_path(B.dims_of(q, ks[0], bt), 0, P) == 1 else "v2"}
             rows.append(rec)
             print(json.dumps(rec), flush=True)
-            del q, k, v, bt, ctx, out, ws
+            del q, ks, vs, bt, ctx, out, ws
     return rows
 
 

@@ -266,9 +266,10 @@ int32_t pa_choose_path(const pa_dims_t* dims, int64_t max_context_len, int32_t p
 
 /* V1/V2 rule.  tokens >= 0: the pages' context-length rule, V1 iff the context
  * bound <= tokens (project_6 commit a2a5dd8 page, decode paths: 8192); 0 means
- * never V1.  tokens < 0 (the default): the rule measured on MI355X -- V1 iff the
- * bound fits in one partition, or S*Hkv >= 256 so that the one-work-group-per-
- * (sequence, KV head) V1 grid already fills the 256 compute units; V2 otherwise.
+ * never V1.  tokens < 0 (the default): the rule measured on MI355X (GPU-side step
+ * times) -- V1 iff the bound is at most 256 tokens, or S*Hkv >= 256 so that the
+ * one-work-group-per-(sequence, KV head) V1 grid already fills the 256 compute
+ * units; V2 otherwise (with fewer sequences V2's work split reaches more units).
  * The environment variable PA_V1_MAX_CONTEXT sets the initial value.  The getter
  * returns -1 for the measured rule.  Process-wide; safe from any thread. */
 void pa_set_v1_max_context(int64_t tokens);
@@ -333,7 +334,7 @@ int32_t pa_get_mfma_variant(void);
  * rule, so the output agrees to rounding).  pa_v2_partition / pa_v2_reduce /
  * pa_v1 never cut.
  * pieces: -1 automatic (default): with C compute units and W items, cut
- *            every item into the most pieces that keep W*pieces <= C when
+ *            every item into the most pieces that keep W*pieces <= 2C when
  *            W < C; else cut the last r = W mod C items (if 0 < r <= C/2)
  *            into the fewest pieces >= 2 that make r*pieces a multiple of C,
  *            or, if none does, into the most pieces allowed;

@@ -25,11 +25,14 @@ thread_local std::string g_last_error;
 
 // V1/V2 choice.  A value >= 0 is a context-length threshold (V1 iff the planning
 // bound is <= it: the rule of project_6 commit a2a5dd8 page, decode paths, where it is
-// 8192).  The default -1 selects the rule measured on MI355X: V1 iff the bound fits
-// one partition, or the V1 grid (one work-group per sequence and KV head) alone
-// already fills the device; otherwise V2.
+// 8192).  The default -1 selects the rule measured on MI355X (GPU-side step times,
+// graph replay, GQA 8, head_dim 128, bf16): V1 iff the bound is at most 256 tokens, or
+// the V1 grid (one work-group per sequence and KV head) alone already fills the device;
+// otherwise V2.  (At 512 tokens and up to 16 sequences V2 is faster: its work split
+// reaches more compute units than V1's S*Hkv work-groups.)
 constexpr int64_t kMeasuredRule = -1;
 constexpr int64_t kV1FillWorkgroups = 256;  // MI355X compute units
+constexpr int64_t kV1MaxShortContext = 256;
 
 std::atomic<int64_t>& v1_threshold() {
   static std::atomic<int64_t> t([] {
@@ -272,8 +275,10 @@ int floor_log2(int64_t x) {
 // dispatched round-robin over them (measured on MI355X: a CU's HBM bandwidth is capped
 // far below what the whole device can stream, so the time of a launch follows the
 // most-loaded CUs):
-//   W <  C: every item is cut into the largest 2^s pieces with W * 2^s <= C, so that a
-//           small grid still reaches every compute unit;
+//   W <  C: every item is cut into the largest 2^s pieces with W * 2^s <= 2C, so that a
+//           small grid still reaches every compute unit (two one-wave work-groups per
+//           unit measured faster than one two-wave one: 8K tokens x 4 KV heads,
+//           10.9 vs 11.3 us/step);
 //   W >= C: the last r = W mod C items, if 0 < r <= C/2, are cut into the fewest
 //           2^s >= 2 pieces with r * 2^s a multiple of C, so that every CU ends with
 //           the same load; failing that, into the most pieces allowed.  (With r > C/2
@@ -295,7 +300,7 @@ pa_status_t plan_split(const Plan& pl, pa::Split* sp) {
     pa_status_t st = compute_units(&ncu);
     if (st != PA_OK) return st;
     if (items < ncu) {
-      shift = std::min(floor_log2(ncu / items), msh);
+      shift = std::min(floor_log2(2 * (int64_t)ncu / items), msh);
       first = 0;
     } else {
       const int64_t rem = items % ncu;
@@ -482,9 +487,10 @@ pa_status_t scratch_address(hipStream_t stream, void** out) {
 int32_t choose(const Plan& pl, int32_t partition_size) {
   const int64_t t = v1_threshold().load();
   if (t >= 0) return pl.ctx_bound <= t ? PA_PATH_V1 : PA_PATH_V2;
-  const bool one_partition = partition_size > 0 && pl.ctx_bound <= partition_size;
+  (void)partition_size;
+  const bool short_context = pl.ctx_bound <= kV1MaxShortContext;
   const bool v1_fills = (int64_t)pl.S * pl.Hkv >= kV1FillWorkgroups;
-  return (one_partition || v1_fills) ? PA_PATH_V1 : PA_PATH_V2;
+  return (short_context || v1_fills) ? PA_PATH_V1 : PA_PATH_V2;
 }
 
 // Whether a V2 call with this plan and split runs as a single launch (given a

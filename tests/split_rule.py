@@ -33,7 +33,7 @@ def plan(items, P, pieces, first_item=0, ncu=None):
         first = min(max(first_item, 0), items)
     else:
         if items < ncu:
-            shift = min((ncu // items).bit_length() - 1, msh)
+            shift = min((2 * ncu // items).bit_length() - 1, msh)
             first = 0
         else:
             rem = items % ncu

@@ -250,14 +250,15 @@ def test_path_rules():
         assert B.pa_choose_path(dims(max_blocks_per_seq=6250), 4000) == B.PA_PATH_V1
         B.pa_set_v1_max_context(0)
         assert B.pa_choose_path(dims(max_blocks_per_seq=1)) == B.PA_PATH_V2
-        # Measured MI355X rule (default): V1 iff one partition or S*Hkv >= 256.
+        # Measured MI355X rule (default): V1 iff the bound is <= 256 tokens or S*Hkv >= 256.
         B.pa_set_v1_max_context(-5)
         assert B.pa_get_v1_max_context() == -1
         one = dims(num_seqs=1, num_kv_heads=4, max_blocks_per_seq=512)            # 8192 tokens
         assert B.pa_choose_path(one, 0, 512) == B.PA_PATH_V2
-        assert B.pa_choose_path(one, 512, 512) == B.PA_PATH_V1                    # one partition
-        assert B.pa_choose_path(one, 513, 512) == B.PA_PATH_V2
-        assert B.pa_choose_path(one, 1024, 1024) == B.PA_PATH_V1
+        assert B.pa_choose_path(one, 256, 512) == B.PA_PATH_V1                    # short
+        assert B.pa_choose_path(one, 257, 512) == B.PA_PATH_V2
+        assert B.pa_choose_path(one, 512, 512) == B.PA_PATH_V2                    # one partition
+        assert B.pa_choose_path(one, 1024, 1024) == B.PA_PATH_V2
         wide = dims(num_seqs=64, num_kv_heads=4, max_blocks_per_seq=6250)         # 256 KV heads
         assert B.pa_choose_path(wide, 0, 512) == B.PA_PATH_V1
         narrow = dims(num_seqs=63, num_kv_heads=4, max_blocks_per_seq=6250)       # 252
@@ -343,9 +344,10 @@ def test_split_rule_examples():
     assert split_rule.plan(896, 512, -1, ncu=256) == (768, 2, 1024)    # remainder 128
     assert split_rule.plan(960, 512, -1, ncu=256) == (960, 1, 960)     # remainder 192 > 128
     assert split_rule.plan(868, 512, -1, ncu=256) == (768, 8, 1568)    # 100: no multiple
-    assert split_rule.plan(64, 512, -1, ncu=256) == (0, 4, 256)        # 8K tokens, 4 KV heads
+    assert split_rule.plan(64, 512, -1, ncu=256) == (0, 8, 512)        # 8K tokens, 4 KV heads
+    assert split_rule.plan(128, 512, -1, ncu=256) == (0, 4, 512)       # 16K tokens
+    assert split_rule.plan(200, 512, -1, ncu=256) == (0, 2, 400)
     assert split_rule.plan(2, 512, -1, ncu=256) == (0, 8, 16)
-    assert split_rule.plan(200, 512, -1, ncu=256) == (200, 1, 200)     # 256/200 < 2
     assert split_rule.plan(64, 64, -1, ncu=256) == (64, 1, 64)         # P = 64: no pieces
     assert split_rule.plan(8192, 512, -1, ncu=256) == (8192, 1, 8192)  # 32 per CU
     assert split_rule.plan(257, 256, -1, ncu=256) == (256, 4, 260)     # P = 256: at most 4
