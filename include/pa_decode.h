@@ -423,12 +423,33 @@ pa_status_t pa_prefill(const pa_prefill_dims_t* dims, void* out, const void* q,
                        const int32_t* context_lens, const int32_t* query_start, float scale,
                        void* stream);
 /* pa_prefill plus start / stop timestamps (hipEvent_t, may be NULL) recorded by the
- * runtime when the prefill kernel starts and ends. */
+ * runtime when the prefill kernel starts and when the call's last kernel ends (bf16 in
+ * mode 0: the recompute launch, see pa_set_prefill_mode). */
 pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const void* q,
                                 const void* k_new, const void* v_new, const void* k_cache,
                                 const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start,
                                 float scale, void* stream, void* start_event, void* stop_event);
+
+/* How pa_prefill feeds the probabilities P to the PV products (the matrix cores take
+ * 16-bit operands).  Process-wide; env PA_PREFILL_MODE sets the initial value.
+ *   0 (default): P as one fp16 value (11 significant bits) and V as fp16; bf16 V is
+ *     converted when staged, exactly for |v| < 65536 (below fp16's normal range the
+ *     absolute error is at most 2^-25).  For bf16 each call then makes a second
+ *     launch that returns at once unless the first one ended with a non-finite
+ *     accumulator somewhere (a V value beyond fp16's range becomes an infinity there;
+ *     non-finite inputs do the same); in that case it recomputes the whole call as in
+ *     mode 1.
+ *   1: P as a 16-bit high part plus a 16-bit low part in the input type (about 16
+ *     significant bits), V as given; twice the PV products.
+ * Both meet |out - ref| <= 2e-3 + 1e-2 |ref| against exact attention for N(0, 1)
+ * inputs at scales up to 0.5; P rounded to bf16 alone does not.  The overflow marks
+ * of mode 0 live in 1024 words of static device memory, one per call (round robin):
+ * a call's mark can be lost only if 1024 later bf16 calls on the same device are
+ * enqueued before its recompute launch runs.  Returns PA_ERR_UNSUPPORTED for another
+ * mode. */
+pa_status_t pa_set_prefill_mode(int32_t mode);
+int32_t pa_get_prefill_mode(void);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -87,6 +87,8 @@ SIGNATURES = {
     "pa_get_mfma_variant": (_I32, []),
     "pa_set_fused": (_I32, [_I32]),
     "pa_get_fused": (_I32, []),
+    "pa_set_prefill_mode": (_I32, [_I32]),
+    "pa_get_prefill_mode": (_I32, []),
     "pa_fused_applies": (_I32, [_DIMS, _I32]),
     "pa_set_work_split": (_I32, [_I32, _I64]),
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
@@ -345,6 +347,16 @@ def pa_set_fused(mode):
 
 def pa_get_fused():
     return int(lib().pa_get_fused())
+
+
+def pa_set_prefill_mode(mode):
+    """0: P and V as fp16 in prefill's PV products (bf16 recomputed in the two-part form
+    when V does not fit fp16); 1: P as a 16-bit high plus low part (process-wide)."""
+    _check(lib().pa_set_prefill_mode(int(mode)))
+
+
+def pa_get_prefill_mode():
+    return int(lib().pa_get_prefill_mode())
 
 
 def pa_fused_applies(q, k_cache, block_tables, partition_size=512):

@@ -227,6 +227,22 @@ pa_status_t make_plan(const pa_dims_t* d, int64_t max_context_len, int32_t parti
 // mixed batch, so it is not the default.  Env PA_FUSED sets the initial value.
 std::atomic<int> g_fused{-2};  // -2: not yet read from the environment
 
+// Prefill PV form (see pa_set_prefill_mode): 0 one fp16 part (with the two-part
+// recompute for bf16 V beyond fp16's range), 1 always two parts.  Env PA_PREFILL_MODE
+// sets the initial value.
+std::atomic<int> g_prefill_mode{-2};
+
+int prefill_mode_setting() {
+  int v = g_prefill_mode.load(std::memory_order_relaxed);
+  if (v == -2) {
+    v = 0;
+    const char* e = std::getenv("PA_PREFILL_MODE");
+    if (e && (e[0] == '0' || e[0] == '1') && e[1] == '\0') v = e[0] - '0';
+    g_prefill_mode.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 int fused_setting() {
   int v = g_fused.load(std::memory_order_relaxed);
   if (v == -2) {
@@ -641,6 +657,7 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   a.Hkv = d->num_kv_heads;
   a.NB = d->num_blocks;
   a.MB = d->max_blocks_per_seq;
+  a.precise = prefill_mode_setting();
   return hip_status(pa::launch_prefill(d->dtype, G, d->head_dim, a, d->num_seqs, maxq,
                                        static_cast<hipStream_t>(stream), e0, e1),
                     "prefill launch");
@@ -916,6 +933,15 @@ pa_status_t pa_set_fused(int32_t mode) {
 }
 
 int32_t pa_get_fused(void) { return fused_setting(); }
+
+pa_status_t pa_set_prefill_mode(int32_t mode) {
+  if (mode < 0 || mode > 1)
+    return fail(PA_ERR_UNSUPPORTED, "prefill mode %d unknown (0 or 1)", mode);
+  g_prefill_mode.store(mode, std::memory_order_relaxed);
+  return ok();
+}
+
+int32_t pa_get_prefill_mode(void) { return prefill_mode_setting(); }
 
 pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item) {
   if (pieces != -1 && pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4 && pieces != 8 &&

@@ -149,10 +149,25 @@ struct PrefillArgs {
   // > 0: the number of sequences S; work-group z then takes the sequence of rank z in
   // most-keys-first order (prefix plus new tokens), and position blocks run last first.
   int32_t order_seqs = 0;
+  // 1: P enters the PV products as a 16-bit high part plus a 16-bit low part (in the
+  // input type).  0: as one fp16 part, with V in fp16 too (bf16 V converted when it is
+  // written to LDS); for bf16 a second launch then recomputes the call in the two-part
+  // form if some V value did not fit fp16 (see prefill_overflow_flags).
+  int32_t precise = 0;
+  // Set by launch_prefill: the overflow word of this call (flags[epoch % kPrefillFlagSlots]
+  // == epoch after an overflow) and, in the recompute launch, flag_check = 1.
+  uint32_t* flags = nullptr;
+  uint32_t epoch = 0;
+  int32_t flag_check = 0;
 };
+constexpr int kPrefillFlagSlots = 1024;
 // Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128 or 256,
-// fp16/bf16.  e0 / e1 (may be null) are recorded when the kernel starts / ends.
+// fp16/bf16.  e0 / e1 (may be null) are recorded when the first kernel starts / the last
+// one ends (bf16 one-part form: the prefill kernel, then the recompute launch).
 hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& a, int num_seqs,
                           int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1);
+// The current device's overflow words (kPrefillFlagSlots of them, in static device memory)
+// and a fresh call number (never 0) for the one-part bf16 prefill.
+hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch);
 
 }  // namespace pa

@@ -31,15 +31,25 @@
 //                  accumulators of the two blocks are exactly the A operand (k-slot e of
 //                  lane group kg is key 16(2s + e/4) + 4kg + e%4); the B operand comes
 //                  from V in LDS through the gfx950 transposing read, in that key order.
-//                  P goes in as a 16-bit high part and a 16-bit low part (the rounding
-//                  residual), one product each, so that p keeps about 16 significant
-//                  bits; the row sums of P add exactly those values (on the VALU).
+//                  P goes in as one fp16 value (11 significant bits), and V as fp16 too:
+//                  bf16 V is converted when it is written to LDS, exactly for every
+//                  |v| < 65536 (bf16's 8-bit significand fits fp16's 11; below fp16's
+//                  normal range the absolute error is at most 2^-25).  A value that does
+//                  not fit is noted, and the call is recomputed by a second launch with P
+//                  as a 16-bit high part plus a 16-bit low part in the input type (about
+//                  16 significant bits, V unconverted).  bf16 P alone (8 bits) is not
+//                  enough: with peaky softmax rows the rounding of P moves outputs near
+//                  zero by more than the 2e-3 absolute tolerance.  The row sums of P add
+//                  exactly the values the products use (on the VALU).
 // K and V have two LDS buffers each; a tile's K is written one phase before its first
 // QK^T and its V one phase before its first PV, from loads issued two phases earlier.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 
 #include "pa_decode.h"
@@ -188,18 +198,30 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
 
 // kOrder: the most-keys-first order above (launches with several sequences); a separate
 // instantiation, so the one-sequence kernel's register allocation is untouched.
-template <int DT, int G, int D, bool kOrder>
+// kPrec: P as a high plus a low part in the input type (else one fp16 part, see the top
+// of the file); with a.flag_check the kernel computes only if this call's overflow word
+// is set.
+template <int DT, int G, int D, bool kOrder, bool kPrec>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
+  constexpr bool kPvBF = kBF && kPrec;  // PV operand type: bf16, else fp16
+  constexpr bool kCvtV = kBF && !kPrec;  // bf16 V converted to fp16 in LDS
+  if constexpr (kPrec) {
+    if (a.flag_check && a.flags[a.epoch % kPrefillFlagSlots] != a.epoch) return;
+  }
   using Sh = Shape<D>;
   constexpr int CG = Sh::CG, KK = Sh::KK, JD = Sh::JD, ROW = Sh::ROW, XC = Sh::XC;
   constexpr int kPos = Sh::ROWS / G;  // query positions per work-group
   __shared__ u32x4 s_k[2][kTile * ROW];
   __shared__ u32x4 s_v[2][kTile * ROW];
   __shared__ int s_pick;
-  // At head_dim 128 the query operands live in LDS, each wave's in lane order (16-byte
-  // reads, conflict-free): the two-part P of the PV product needs the registers.
-  constexpr bool kQLds = D == 128;
+  // At head_dim 128 the two-part form keeps the query operands in LDS, each wave's in
+  // lane order (16-byte reads, conflict-free): its low parts of P need the registers.
+  constexpr bool kQLds = kPrec && D == 128;
+  // Row sums of P: in the one-part form on the matrix cores (one more product per column
+  // group and key step, with an all-ones B operand, leaves sum_k P[row][k] in every
+  // column, in O's row layout); in the two-part form on the VALU (high plus low parts).
+  constexpr bool kSumMfma = !kPrec && D == 128;  // measured: MFMA at 128, VALU at 256
   __shared__ u32x4 s_q[kQLds ? 8 : 1][kQLds ? CG * KK : 1][64];
 
   const int g = blockIdx.y;
@@ -271,11 +293,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // own keys (4 kg + i of every 16-key row block); the four lane groups are summed at
   // the end.
   float lsum[CG];
+  f32x4 Lacc[kSumMfma ? CG : 1];
+  const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0
   float m_ref[CG];
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     m_ref[cg] = kNegInf;
     lsum[cg] = 0.f;
+    if constexpr (kSumMfma) Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- tile loads: thread tid moves XC chunks (lc, lc + 8, ...) of K and of V of tile row tid/8 ----
@@ -323,13 +348,31 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 #pragma unroll
     for (int i = 0; i < XC; ++i) dst[lrow * ROW + lc + 8 * i] = ok ? r[i] : z;
   };
+  // V rows as the PV products take them: bf16 converted to fp16 in the one-part form (a
+  // value beyond fp16's range becomes an infinity; see the end of the kernel).
+  auto store_v = [&](u32x4* dst, const u32x4 (&r)[XC], bool ok) {
+    if constexpr (kCvtV) {
+      u32x4 c[XC];
+#pragma unroll
+      for (int i = 0; i < XC; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = r[i][e];
+          c[i][e] = pack2<false>(__builtin_bit_cast(float, wv << 16),
+                                 __builtin_bit_cast(float, wv & 0xffff0000u));
+        }
+      store_rows(dst, c, ok);
+    } else {
+      store_rows(dst, r, ok);
+    }
+  };
 
   {
     const int blk0 = fetch_block(0);
     load_k(0, blk0);
     load_v(0, blk0);
     store_rows(s_k[0], kr, ok_k);
-    store_rows(s_v[0], vr, ok_v);
+    store_v(s_v[0], vr, ok_v);
   }
   int blk_k = fetch_block(1), blk_v = blk_k;
   load_k(1, blk_k);
@@ -340,8 +383,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 
   f32x4 S[4][CG];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
   // [cg][st]: P of the tile as PV A operands (keys of row blocks 2st, 2st+1), as the
-  // 16-bit high parts (P) and low parts (Pl).
-  u32x4 P[CG][2], Pl[CG][2];
+  // 16-bit high parts (P) and, in the two-part form, low parts (Pl).
+  u32x4 P[CG][2], Pl[kPrec ? CG : 1][2];
 
   // S^T of tile t.
   auto qk = [&](int t) {
@@ -392,32 +435,55 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         const u32x2 hi = lds_read_tr(src + 16 * ROW * 16);
         vb[st][jd] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-    // Per pair of 16-column blocks: the high-part products of both blocks and every
-    // column group, then the low-part ones, so a product never waits for the one just
-    // issued on the same accumulator.
+    if constexpr (kPrec) {
+      // Per pair of 16-column blocks: the high-part products of both blocks and every
+      // column group, then the low-part ones, so a product never waits for the one just
+      // issued on the same accumulator.
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int jd = 0; jd < JD; jd += 2) {
+        for (int jd = 0; jd < JD; jd += 2) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int cg = 0; cg < CG; ++cg)
-            O[cg][jd + jj] = mfma32<kBF>(P[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
+            for (int cg = 0; cg < CG; ++cg)
+              O[cg][jd + jj] = mfma32<kPvBF>(P[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int cg = 0; cg < CG; ++cg)
-            O[cg][jd + jj] = mfma32<kBF>(Pl[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
+            for (int cg = 0; cg < CG; ++cg)
+              O[cg][jd + jj] = mfma32<kPvBF>(Pl[cg][st], vb[st][jd + jj], O[cg][jd + jj]);
+        }
+      // V reads (two per operand) run two operands ahead of the products that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * JD - 2; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * CG, 0);
       }
-    // V reads (two per operand) run two operands ahead of the products that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 2 * JD - 2; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * CG, 0);
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int jd = 0; jd < JD; ++jd)
+#pragma unroll
+          for (int cg = 0; cg < CG; ++cg)
+            O[cg][jd] = mfma32<false>(P[cg][st], vb[st][jd], O[cg][jd]);
+        if constexpr (kSumMfma) {
+#pragma unroll
+          for (int cg = 0; cg < CG; ++cg) Lacc[cg] = mfma32<false>(P[cg][st], ones, Lacc[cg]);
+        }
+      }
+      // V reads (two per operand) run four operands ahead of the products that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * JD - 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, CG, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, (kSumMfma ? 6 : 4) * CG, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * CG, 0);
   };
   // Softmax of tile t: row max (masked keys become -inf on diagonal tiles, where S then
   // holds scaled logits), the rescale of O when a row max grows past the slack, and P.
@@ -459,10 +525,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[cg][j][i] *= al[i];
         lsum[cg] *= alpha;  // this lane's sums are of row r16, the row alpha belongs to
+        if constexpr (kSumMfma) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Lacc[cg][i] *= al[i];
+        }
       }
     }
     // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
+    const f16x2 ones2 = {(_Float16)1.f, (_Float16)1.f};  // one-part row sums: p0 + p1 + sum
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       const float nm = -m_ref[cg];
@@ -477,14 +548,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hw[e] = pack2<kBF>(p[2 * e], p[2 * e + 1]);
-          const float h0 = unpack_lo<kBF>(hw[e]), h1 = unpack_hi<kBF>(hw[e]);
-          lw[e] = pack2<kBF>(p[2 * e] - h0, p[2 * e + 1] - h1);
-          part += (h0 + unpack_lo<kBF>(lw[e])) + (h1 + unpack_hi<kBF>(lw[e]));
+          hw[e] = pack2<kPvBF>(p[2 * e], p[2 * e + 1]);
+          if constexpr (kPrec) {
+            const float h0 = unpack_lo<kPvBF>(hw[e]), h1 = unpack_hi<kPvBF>(hw[e]);
+            lw[e] = pack2<kPvBF>(p[2 * e] - h0, p[2 * e + 1] - h1);
+            part += (h0 + unpack_lo<kPvBF>(lw[e])) + (h1 + unpack_hi<kPvBF>(lw[e]));
+          } else if constexpr (!kSumMfma) {
+            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[e]), ones2, part, false);
+          }
         }
-        lsum[cg] += part;
+        if constexpr (!kSumMfma) lsum[cg] += part;
         P[cg][st] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-        Pl[cg][st] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        if constexpr (kPrec) Pl[cg][st] = u32x4{lw[0], lw[1], lw[2], lw[3]};
       }
     }
   };
@@ -505,7 +580,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     blk_k = fetch_block(u + 3);
   };
   auto io_v = [&](int u) {
-    store_rows(s_v[(u + 1) & 1], vr, ok_v);
+    store_v(s_v[(u + 1) & 1], vr, ok_v);
     load_v(u + 2, blk_v);
     blk_v = fetch_block(u + 3);
   };
@@ -543,13 +618,30 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 #undef PA_TILE
 
+  // A V value fp16 does not hold was staged as an infinity, and the PV products carry it
+  // into its head-dim column of O in every row of the work-group (as +-inf, or NaN where
+  // p = 0): a non-finite accumulator marks this call for the two-part recompute.  So do
+  // non-finite inputs and an fp32 overflow of O, which the recompute then meets as well.
+  if constexpr (kCvtV) {
+    bool bad = false;
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+      for (int j = 0; j < JD; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(O[cg][j][i]);
+    if (bad)
+      __hip_atomic_store(a.flags + a.epoch % kPrefillFlagSlots, a.epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
-    const float lrow = sum_over_groups(lsum[cg]);  // row r16's sum, in every lane group
+    const float lrow = kSumMfma ? 0.f : sum_over_groups(lsum[cg]);  // row r16's sum
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(lrow, 4 * kg + i);
+      const float li = kSumMfma ? Lacc[cg][i] : __shfl(lrow, 4 * kg + i);
       const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
       const int pos = p0 + row / G;
       if (pos >= L) continue;
@@ -566,19 +658,26 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 }
 
-template <int DT, int D, bool kOrder>
+template <int DT, int D, bool kOrder, bool kPrec>
 hipError_t launch_gg(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
                      hipEvent_t e1) {
   const dim3 block(kThreads);
   switch (G) {
-    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kOrder>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int DT, int D, bool kPrec>
+hipError_t launch_p(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
+                    hipEvent_t e1) {
+  if (a.order_seqs > 0) return launch_gg<DT, D, true, kPrec>(G, grid, a, st, e0, e1);
+  return launch_gg<DT, D, false, kPrec>(G, grid, a, st, e0, e1);
 }
 
 template <int DT, int D>
@@ -588,14 +687,67 @@ hipError_t launch_g(int G, const PrefillArgs& a, int num_seqs, int max_query_len
   const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
   PrefillArgs ao = a;
   ao.order_seqs = num_seqs >= 2 && num_seqs <= kOrderMaxSeqs ? num_seqs : 0;
-  if (ao.order_seqs > 0) return launch_gg<DT, D, true>(G, grid, ao, st, e0, e1);
-  return launch_gg<DT, D, false>(G, grid, ao, st, e0, e1);
+  ao.flag_check = 0;
+  if (a.precise) return launch_p<DT, D, true>(G, grid, ao, st, e0, e1);
+  if constexpr (DT != PA_BF16) {
+    return launch_p<DT, D, false>(G, grid, ao, st, e0, e1);
+  } else {
+    // One-part form, then the two-part recompute, which runs only if the first launch
+    // marked this call's overflow word.
+    hipError_t err = launch_p<DT, D, false>(G, grid, ao, st, e0, nullptr);
+    if (err != hipSuccess) return err;
+    ao.flag_check = 1;
+    return launch_p<DT, D, true>(G, grid, ao, st, nullptr, e1);
+  }
 }
+
+// Overflow words of the one-part bf16 form: call e (a number the host draws from a
+// 32-bit counter, never 0) owns word e % kPrefillFlagSlots and marks an overflow by
+// storing e there; the recompute launch of the same call compares the word with e.  A
+// word that still holds e from an earlier run of the same launches (a replayed graph)
+// only makes the recompute run when it was not needed.  A call's overflow can be missed
+// only if kPrefillFlagSlots later calls on the same device are issued while it is still
+// in flight.  In host code `prefill_flag_words` names a host-side stand-in: the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint32_t prefill_flag_words[kPrefillFlagSlots];
 
 }  // namespace
 
-hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& a, int num_seqs,
-                          int max_query_len, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+namespace {
+constexpr int kFlagDevices = 64;
+std::mutex g_flag_mutex;
+uint32_t* g_flag_ptr[kFlagDevices] = {};
+std::atomic<uint32_t> g_epoch{0};
+}  // namespace
+
+hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kFlagDevices) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(g_flag_mutex);
+    if (!g_flag_ptr[dev]) {
+      void* p = nullptr;
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(prefill_flag_words));
+      if (err != hipSuccess) return err;
+      if (!p) return hipErrorInvalidSymbol;
+      g_flag_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    *words = g_flag_ptr[dev];
+  }
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  *epoch = e;
+  return hipSuccess;
+}
+
+hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& args,
+                          int num_seqs, int max_query_len, hipStream_t stream, hipEvent_t e0,
+                          hipEvent_t e1) {
+  PrefillArgs a = args;
+  const hipError_t err = prefill_overflow_flags(&a.flags, &a.epoch);  // valid in every launch
+  if (err != hipSuccess) return err;
   if (head_dim == 128)
     return dtype == PA_BF16 ? launch_g<PA_BF16, 128>(group, a, num_seqs, max_query_len, stream, e0, e1)
          : dtype == PA_F16  ? launch_g<PA_F16, 128>(group, a, num_seqs, max_query_len, stream, e0, e1)

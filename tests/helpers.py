@@ -81,6 +81,18 @@ def fused_mode(mode):
 
 
 @contextlib.contextmanager
+def prefill_mode(mode):
+    """Run the block with the library's prefill PV form changed, then restore it."""
+    from paged_split_kv_pa_amd import binding as B
+    old = B.pa_get_prefill_mode()
+    B.pa_set_prefill_mode(mode)
+    try:
+        yield
+    finally:
+        B.pa_set_prefill_mode(old)
+
+
+@contextlib.contextmanager
 def work_split(pieces, first_item=0):
     """Run the block with the library's work-split setting changed, then restore it."""
     from paged_split_kv_pa_amd import binding as B

@@ -450,3 +450,17 @@ def test_prefill_pointers_and_empty_calls():
     nul = [ctypes.c_void_p(0)] * 9
     assert lib.pa_prefill(ctypes.byref(pdims(num_tokens=0)), *nul, 0.1, None) == 0
     assert lib.pa_prefill(ctypes.byref(pdims(num_seqs=0)), *nul, 0.1, None) == 0
+
+
+def test_prefill_mode_knob():
+    old = B.pa_get_prefill_mode()
+    try:
+        for m in (1, 0):
+            B.pa_set_prefill_mode(m)
+            assert B.pa_get_prefill_mode() == m
+        for bad in (-1, 2):
+            with pytest.raises(B.PaError):
+                B.pa_set_prefill_mode(bad)
+        assert B.pa_get_prefill_mode() == 0
+    finally:
+        B.pa_set_prefill_mode(old)
