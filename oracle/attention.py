@@ -192,9 +192,9 @@ def merge_partials(a, b):
 
     ``a`` and ``b`` are ``(max_logit, exp_sum, normalised_out)``; the identity is
     ``(-inf, 0, 0)``.  m = max(m1, m2), a_i = exp(m_i - m) s_i, result =
-    (m, a_1 + a_2, (a_1 o_1 + a_2 o_2) / (a_1 + a_2)).  This is the
-    "combine partial statistics from independent segments" pattern named on
-    the project_6 commit 96f4baf page; folding it over partitions gives Phase 2.
+    (m, a_1 + a_2, (a_1 o_1 + a_2 o_2) / (a_1 + a_2)).  The project_6 commit
+    96f4baf page (V2 plan) likens Phase 2 to merging softmax statistics computed
+    on separate segments; folding this merge over the partitions gives Phase 2.
     """
     m1, s1, o1 = a
     m2, s2, o2 = b
