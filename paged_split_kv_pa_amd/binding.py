@@ -89,6 +89,8 @@ SIGNATURES = {
     "pa_get_fused": (_I32, []),
     "pa_set_prefill_mode": (_I32, [_I32]),
     "pa_get_prefill_mode": (_I32, []),
+    "pa_set_prefill_split": (_I32, [_I32]),
+    "pa_get_prefill_split": (_I32, []),
     "pa_fused_applies": (_I32, [_DIMS, _I32]),
     "pa_set_work_split": (_I32, [_I32, _I64]),
     "pa_get_work_split": (_I32, [ctypes.POINTER(_I64)]),
@@ -357,6 +359,16 @@ def pa_set_prefill_mode(mode):
 
 def pa_get_prefill_mode():
     return int(lib().pa_get_prefill_mode())
+
+
+def pa_set_prefill_split(chunk_tiles):
+    """Prefill load balance: -1 automatic chunks (default), 0 none, k >= 4 chunks of at
+    most k 64-key tiles (process-wide)."""
+    _check(lib().pa_set_prefill_split(int(chunk_tiles)))
+
+
+def pa_get_prefill_split():
+    return int(lib().pa_get_prefill_split())
 
 
 def pa_fused_applies(q, k_cache, block_tables, partition_size=512):

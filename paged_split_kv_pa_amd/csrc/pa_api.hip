@@ -232,6 +232,26 @@ std::atomic<int> g_fused{-2};  // -2: not yet read from the environment
 // sets the initial value.
 std::atomic<int> g_prefill_mode{-2};
 
+// Prefill chunk setting (see pa_set_prefill_split): -1 automatic, 0 the non-planned grid,
+// >= pa::kPrefillMinChunk a fixed chunk length in tiles.  Env PA_PREFILL_SPLIT.
+std::atomic<int> g_prefill_split{-2};
+
+int prefill_split_setting() {
+  int v = g_prefill_split.load(std::memory_order_relaxed);
+  if (v == -2) {
+    v = -1;
+    const char* e = std::getenv("PA_PREFILL_SPLIT");
+    if (e && *e) {
+      char* end = nullptr;
+      const long x = std::strtol(e, &end, 10);
+      if (end && *end == '\0' && (x == -1 || x == 0 || (x >= pa::kPrefillMinChunk && x <= (1 << 20))))
+        v = (int)x;
+    }
+    g_prefill_split.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 int prefill_mode_setting() {
   int v = g_prefill_mode.load(std::memory_order_relaxed);
   if (v == -2) {
@@ -658,6 +678,27 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   a.NB = d->num_blocks;
   a.MB = d->max_blocks_per_seq;
   a.precise = prefill_mode_setting();
+  a.max_query_len = maxq;
+  a.chunk = prefill_split_setting();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!a.precise && a.chunk != 0 && d->num_seqs <= pa::kOrderMaxSeqs) {
+    int ncu = 0;
+    if ((st = compute_units(&ncu)) != PA_OK) return st;
+    a.ncu = ncu;
+    const size_t bytes = pa::prefill_plan_bytes(d->head_dim, G, d->num_seqs, a);
+    if (bytes > 0) {
+      void* base = nullptr;
+      if ((st = owned_workspace(bytes, hs, &base)) != PA_OK) return st;
+      char* ws = static_cast<char*>(base) + pa::kFusedCounterBytes;
+      const size_t rows = (size_t)pa::prefill_rows(d->head_dim);
+      const size_t o_bytes = align256((size_t)a.slot_bound * rows * d->head_dim * 4);
+      const size_t s_bytes = align256((size_t)a.slot_bound * rows * 4);
+      a.plan = reinterpret_cast<int32_t*>(ws);
+      a.part_o = reinterpret_cast<float*>(ws + align256(sizeof(int32_t) * pa::kPrefillPlanWords));
+      a.part_m = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_o) + o_bytes);
+      a.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_m) + s_bytes);
+    }
+  }
   return hip_status(pa::launch_prefill(d->dtype, G, d->head_dim, a, d->num_seqs, maxq,
                                        static_cast<hipStream_t>(stream), e0, e1),
                     "prefill launch");
@@ -942,6 +983,17 @@ pa_status_t pa_set_prefill_mode(int32_t mode) {
 }
 
 int32_t pa_get_prefill_mode(void) { return prefill_mode_setting(); }
+
+pa_status_t pa_set_prefill_split(int32_t chunk_tiles) {
+  if (chunk_tiles != -1 && chunk_tiles != 0 &&
+      (chunk_tiles < pa::kPrefillMinChunk || chunk_tiles > (1 << 20)))
+    return fail(PA_ERR_UNSUPPORTED, "prefill chunk setting %d unknown (-1, 0 or %d..%d tiles)",
+                chunk_tiles, pa::kPrefillMinChunk, 1 << 20);
+  g_prefill_split.store(chunk_tiles, std::memory_order_relaxed);
+  return ok();
+}
+
+int32_t pa_get_prefill_split(void) { return prefill_split_setting(); }
 
 pa_status_t pa_set_work_split(int32_t pieces, int64_t first_item) {
   if (pieces != -1 && pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4 && pieces != 8 &&

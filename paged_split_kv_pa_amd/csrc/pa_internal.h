@@ -159,8 +159,25 @@ struct PrefillArgs {
   uint32_t* flags = nullptr;
   uint32_t epoch = 0;
   int32_t flag_check = 0;
+  // Planned schedule (see prefill_plan_kernel; one-part form, 1..kOrderMaxSeqs sequences):
+  // the plan table and the partial states of split row blocks in a workspace, the bounds
+  // the host sized them for, the compute-unit count and the chunk setting (-1 automatic,
+  // >= kPrefillMinChunk a fixed chunk length in 64-key tiles; 0: no planned schedule).
+  int32_t* plan = nullptr;
+  float* part_o = nullptr;   // [slot][8 waves][CG][JD][64 lanes] f32x4
+  float* part_m = nullptr;   // [slot][8 waves][CG][16 rows]
+  float* part_l = nullptr;   // [slot][8 waves][CG][16 rows]
+  int32_t max_query_len = 0;
+  int32_t ncu = 0;
+  int32_t chunk = 0;
+  int32_t item_bound = 0, slot_bound = 0, merge_bound = 0;
 };
 constexpr int kPrefillFlagSlots = 1024;
+constexpr int kPrefillMinChunk = 4;       // tiles; a chunk then spans at least 2 tiles
+constexpr int kPrefillAutoMinChunk = 16;  // tiles; the automatic chunk length's floor
+constexpr int kPrefillPlanWords = 8 + 8 * (kOrderMaxSeqs + 1);  // header + records
+// Query rows (position, head) of one prefill work-group.
+constexpr int prefill_rows(int head_dim) { return head_dim == 128 ? 256 : 128; }
 // Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128 or 256,
 // fp16/bf16.  e0 / e1 (may be null) are recorded when the first kernel starts / the last
 // one ends (bf16 one-part form: the prefill kernel, then the recompute launch).
@@ -169,5 +186,8 @@ hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs&
 // The current device's overflow words (kPrefillFlagSlots of them, in static device memory)
 // and a fresh call number (never 0) for the one-part bf16 prefill.
 hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch);
+// Whether a prefill launch takes the planned schedule, and the workspace bytes it needs
+// (0 if it does not); fills the bounds in a (item_bound, slot_bound, merge_bound).
+size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a);
 
 }  // namespace pa

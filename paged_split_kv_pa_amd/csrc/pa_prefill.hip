@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -82,6 +83,9 @@ struct Shape {
   static constexpr int ROW = CH + 2;           // LDS row stride, 16-byte units
   static constexpr int XC = CH / 8;            // chunks of a row one thread stages
 };
+
+static_assert(Shape<128>::ROWS == prefill_rows(128) && Shape<256>::ROWS == prefill_rows(256),
+              "work-group rows as the host sizes the partial states");
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -196,12 +200,236 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
   return *s_pick;
 }
 
-// kOrder: the most-keys-first order above (launches with several sequences); a separate
-// instantiation, so the one-sequence kernel's register allocation is untouched.
+// ---- planned schedule ----------------------------------------------------------------
+// A row block is the work of the non-planned grid's work-group: positions [p0, p0 + kPos)
+// of one sequence and one KV head, over keys [0, c + min(L, p0 + kPos)) in 64-key tiles.
+// Work-groups start in grid order and one runs per compute unit, so a launch whose row
+// blocks differ in length (a long prefix next to short ones, or a few row blocks over a
+// long prefix) ends on its longest row blocks alone.  The planned schedule cuts every
+// row block of more than C tiles into ceil(t / C) chunks of consecutive tiles (C =
+// max(16, ceil(W / 3N)) for W tiles in the launch over N compute units: about three
+// chunks' worth of work per unit), and hands out items longest first: work-group j
+// takes item j of the list
+//   the chunks of the cut row blocks, then the uncut row blocks,
+// each part by sequence in most-keys-first order, then position block last first, then
+// KV head (then chunk).  A chunk writes its (row max, row sum, unnormalised output) to a
+// slot of the workspace (slot = its item index); prefill_merge_kernel folds the chunks
+// of each cut row block with the log-sum-exp rule, in chunk order.  Within a sequence t
+// grows with the position block, so the cut row blocks are those from position block
+// xs on.  A chunk spans at least two tiles; a row that sees no key of a chunk (possible
+// when the chunk starts inside the causal part) leaves (-inf, 0, 0), which the merge
+// weighs by 0.
+//
+// Plan table (int32, in the workspace): header {C, split items S1, items, cut row
+// blocks}, then per rank r (S + 1 records of 8 words; record S holds the totals):
+// {sequence, c, r0, L, xs, split prefix, uncut prefix, cut-row-block prefix}, prefixes
+// counted over KV heads.
+constexpr int kRecWords = 8;
+enum { kRecSeq = 0, kRecC, kRecR0, kRecL, kRecXs, kRecSplit, kRecUncut, kRecCut };
+
+__device__ __forceinline__ int plan_tiles(int c, int L, int xb, int kpos) {
+  return (c + min(L, (xb + 1) * kpos) + kTile - 1) / kTile;
+}
+
+// Exclusive prefix sum over the 512 threads of a work-group (v = 0 past the data);
+// *total receives the sum.  s_tmp: 8 words of LDS.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int x = s_tmp[i];
+    off += i < w ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+// Largest r in [0, n) with rec[r][field] <= key (rec[0][field] == 0 <= key).
+__device__ __forceinline__ int plan_search(const int* rec, int n, int field, int key) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rec[mid * kRecWords + field] <= key) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Position block of the `local`-th cut item (or cut row block) of a sequence, walking
+// position blocks from npb - 1 down to xs, each worth per_xb(xb) items; returns xb and
+// sets *before to the items of the position blocks after it.  Every wave computes the
+// same result (no LDS, no barrier).
+template <typename F>
+__device__ __forceinline__ int plan_walk(int npb, int xs, int local, F per_xb, int* before) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int base = npb - 1; base >= xs; base -= 64) {
+    const int xb = base - lane;
+    const int v = xb >= xs ? per_xb(xb) : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const unsigned long long hit = __ballot(acc + incl > local);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      *before = acc + __shfl(incl - v, l);
+      return base - l;
+    }
+    acc += __shfl(incl, 63);
+  }
+  *before = acc;  // not reached for a local index inside the sequence's items
+  return xs;
+}
+
+// One work-group of 512 threads; S <= kOrderMaxSeqs sequences.
+__global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, int S, int kpos) {
+  __shared__ int s_c[kOrderMaxSeqs], s_r0[kOrderMaxSeqs], s_L[kOrderMaxSeqs];
+  __shared__ int s_npb[kOrderMaxSeqs + 1], s_xs[kOrderMaxSeqs];
+  __shared__ int s_order[kOrderMaxSeqs];
+  __shared__ unsigned long long s_w[kOrderMaxSeqs];
+  __shared__ int s_nsp[kOrderMaxSeqs], s_ncut[kOrderMaxSeqs];
+  __shared__ int s_tmp[8];
+  __shared__ unsigned long long s_wsum;
+  const int tid = threadIdx.x;
+  const int cap = a.MB * kBlockSize;
+  const int maxq = a.max_query_len;
+  int my_npb = 0;
+  if (tid < S) {
+    int r1 = a.query_start[tid + 1], r0 = a.query_start[tid];
+    r1 = min(r1, a.T);
+    r0 = min(max(r0, 0), r1);
+    int c = a.ctx[tid];
+    c = c < 0 ? 0 : (c > cap ? cap : c);
+    s_c[tid] = c;
+    s_r0[tid] = r0;
+    s_L[tid] = r1 - r0;
+    my_npb = (min(r1 - r0, maxq) + kpos - 1) / kpos;
+    s_xs[tid] = my_npb;
+    s_w[tid] = 0;
+    s_nsp[tid] = 0;
+    s_ncut[tid] = 0;
+  }
+  if (tid == 0) s_wsum = 0;
+  int nrb = 0;
+  const int pre = block_exclusive_scan(tid < S ? my_npb : 0, s_tmp, &nrb);
+  if (tid < S) s_npb[tid] = pre;  // exclusive prefix of row blocks per sequence
+  if (tid == 0) s_npb[S] = nrb;
+  __syncthreads();
+  auto seq_of = [&](int p) {  // sequence of flat row block p (s_npb is non-decreasing)
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_npb[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  // Tiles per sequence (one KV head), then W.
+  for (int p = tid; p < nrb; p += blockDim.x) {
+    const int b = seq_of(p);
+    atomicAdd(&s_w[b], (unsigned long long)plan_tiles(s_c[b], s_L[b], p - s_npb[b], kpos));
+  }
+  __syncthreads();
+  if (tid < S) atomicAdd(&s_wsum, s_w[tid]);
+  __syncthreads();
+  const unsigned long long W = s_wsum * (unsigned long long)a.Hkv;
+  const unsigned long long per = 3ull * (unsigned long long)max(a.ncu, 1);
+  long long C = a.chunk > 0 ? a.chunk
+                            : max((long long)kPrefillAutoMinChunk, (long long)((W + per - 1) / per));
+  // Cut counts, first cut position block.
+  for (int p = tid; p < nrb; p += blockDim.x) {
+    const int b = seq_of(p), xb = p - s_npb[b];
+    const long long t = plan_tiles(s_c[b], s_L[b], xb, kpos);
+    const long long n = (t + C - 1) / C;
+    if (n > 1) {
+      atomicAdd(&s_nsp[b], (int)n);
+      atomicAdd(&s_ncut[b], 1);
+      atomicMin(&s_xs[b], xb);
+    }
+  }
+  __syncthreads();
+  // Totals; a plan beyond the sizes the host provided for (not expected) is dropped for
+  // the uncut schedule, which always fits.
+  int tsplit = 0, tuncut = 0, tcut = 0;
+  (void)block_exclusive_scan(tid < S ? s_nsp[tid] : 0, s_tmp, &tsplit);
+  (void)block_exclusive_scan(tid < S ? s_xs[tid] : 0, s_tmp, &tuncut);
+  (void)block_exclusive_scan(tid < S ? s_ncut[tid] : 0, s_tmp, &tcut);
+  const long long H = a.Hkv;
+  if (H * tsplit > a.slot_bound || H * (tsplit + tuncut) > a.item_bound ||
+      H * tcut > a.merge_bound) {
+    C = 0x7fffffff;
+    if (tid < S) {
+      s_nsp[tid] = 0;
+      s_ncut[tid] = 0;
+      s_xs[tid] = my_npb;
+    }
+    __syncthreads();
+  }
+  // Most keys first (prefix plus new tokens; ties by index), as the non-planned order.
+  if (tid < S) {
+    const long long kc = (long long)s_c[tid] + s_L[tid];
+    int rank = 0;
+    for (int k = 0; k < S; ++k) {
+      const long long kk = (long long)s_c[k] + s_L[k];
+      rank += (kk > kc) | ((kk == kc) & (k < tid));
+    }
+    s_order[rank] = tid;
+  }
+  __syncthreads();
+  const int b = tid < S ? s_order[tid] : 0;
+  int nsplit = 0, nuncut = 0, ncut = 0;
+  const int psplit = block_exclusive_scan(tid < S ? a.Hkv * s_nsp[b] : 0, s_tmp, &nsplit);
+  const int puncut = block_exclusive_scan(tid < S ? a.Hkv * s_xs[b] : 0, s_tmp, &nuncut);
+  const int pcut = block_exclusive_scan(tid < S ? a.Hkv * s_ncut[b] : 0, s_tmp, &ncut);
+  int* rec = a.plan + 8;
+  if (tid <= S) {
+    int* r = rec + tid * kRecWords;
+    if (tid < S) {
+      r[kRecSeq] = b;
+      r[kRecC] = s_c[b];
+      r[kRecR0] = s_r0[b];
+      r[kRecL] = s_L[b];
+      r[kRecXs] = s_xs[b];
+      r[kRecSplit] = psplit;
+      r[kRecUncut] = puncut;
+      r[kRecCut] = pcut;
+    } else {
+      r[kRecSeq] = r[kRecC] = r[kRecR0] = r[kRecL] = r[kRecXs] = 0;
+      r[kRecSplit] = nsplit;
+      r[kRecUncut] = nuncut;
+      r[kRecCut] = ncut;
+    }
+  }
+  if (tid == 0) {
+    a.plan[0] = (int)C;
+    a.plan[1] = nsplit;
+    a.plan[2] = nsplit + nuncut;
+    a.plan[3] = ncut;
+  }
+}
+
+// kSched: 0 grid order (grid (position blocks, Hkv, S)); 1 the most-keys-first order
+// above over the same grid; 2 the planned schedule (a one-dimensional grid of items, see
+// prefill_plan_kernel).  Separate instantiations, so the one-sequence kernel's register
+// allocation is untouched by the others.
 // kPrec: P as a high plus a low part in the input type (else one fp16 part, see the top
 // of the file); with a.flag_check the kernel computes only if this call's overflow word
 // is set.
-template <int DT, int G, int D, bool kOrder, bool kPrec>
+template <int DT, int G, int D, int kSched, bool kPrec>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs a) {
   constexpr bool kBF = DT == PA_BF16;
   constexpr bool kPvBF = kBF && kPrec;  // PV operand type: bf16, else fp16
@@ -224,34 +452,91 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   constexpr bool kSumMfma = !kPrec && D == 128;  // measured: MFMA at 128, VALU at 256
   __shared__ u32x4 s_q[kQLds ? 8 : 1][kQLds ? CG * KK : 1][64];
 
-  const int g = blockIdx.y;
-  int b = blockIdx.z, xb = blockIdx.x;
-  if constexpr (kOrder) {
-    // The key counts live in the first K tile buffer, which is not written before the
-    // barrier that ends the ranking.
-    b = seq_of_key_rank(a, a.order_seqs, b, reinterpret_cast<long long*>(s_k[0]), &s_pick);
-    xb = gridDim.x - 1 - blockIdx.x;
-  }
-  const int p0 = xb * kPos;
-  int r1 = a.query_start[b + 1], r0 = a.query_start[b];
-  r1 = min(r1, a.T);
-  r0 = min(max(r0, 0), r1);
-  const int L = r1 - r0;
-  if (p0 >= L) return;
-  int c = a.ctx[b];
-  const int cap = a.MB * kBlockSize;
-  c = c < 0 ? 0 : (c > cap ? cap : c);
-
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2;  // 0: matrix phases on even phase numbers, 1: on odd ones
   const int lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
 
+  int g, b, xb, r0, L, c;
+  // Tiles [tb, tb + ntiles) of the row block (all of them unless it is cut), chunk k of
+  // nch; a cut row block's chunk writes its partial state to slot `slot`.
+  int tb = 0, ntiles, nch = 1, slot = 0;
+  if constexpr (kSched == 2) {
+    // The plan table lives in the second V tile buffer until the first barrier of the
+    // tile loop (that buffer is first written after it).
+    int* s_tab = reinterpret_cast<int*>(s_v[1]);
+    const int S = a.order_seqs;
+    for (int i = tid; i < 8 + kRecWords * (S + 1); i += kThreads) s_tab[i] = a.plan[i];
+    __syncthreads();
+    const int j = blockIdx.x;
+    const int C = s_tab[0], S1 = s_tab[1];
+    if (j >= s_tab[2]) return;
+    const int* rec = s_tab + 8;
+    const bool cut = j < S1;
+    const int key = cut ? j : j - S1;
+    const int r = plan_search(rec, S, cut ? kRecSplit : kRecUncut, key);
+    const int* rr = rec + r * kRecWords;
+    b = rr[kRecSeq];
+    c = rr[kRecC];
+    r0 = rr[kRecR0];
+    L = rr[kRecL];
+    const int xs = rr[kRecXs];
+    const int local = key - rr[cut ? kRecSplit : kRecUncut];
+    if (cut) {
+      const int npb = (min(L, a.max_query_len) + kPos - 1) / kPos;
+      const int H = a.Hkv;
+      int before = 0;
+      xb = plan_walk(npb, xs, local,
+                     [&](int x) { return H * ((plan_tiles(c, L, x, kPos) + C - 1) / C); },
+                     &before);
+      nch = (plan_tiles(c, L, xb, kPos) + C - 1) / C;
+      const int rem = local - before;
+      g = rem / nch;
+      const int k = rem - g * nch;
+      const int t_all = plan_tiles(c, L, xb, kPos);
+      tb = k * t_all / nch;
+      ntiles = (k + 1) * t_all / nch - tb;
+      slot = j;
+    } else {
+      xb = xs - 1 - local / a.Hkv;
+      g = local % a.Hkv;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    g = __builtin_amdgcn_readfirstlane(g);
+    xb = __builtin_amdgcn_readfirstlane(xb);
+    c = __builtin_amdgcn_readfirstlane(c);
+    L = __builtin_amdgcn_readfirstlane(L);
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    tb = __builtin_amdgcn_readfirstlane(tb);
+    nch = __builtin_amdgcn_readfirstlane(nch);
+    if (nch > 1) ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+  } else {
+    g = blockIdx.y;
+    b = blockIdx.z;
+    xb = blockIdx.x;
+    if constexpr (kSched == 1) {
+      // The key counts live in the first K tile buffer, which is not written before the
+      // barrier that ends the ranking.
+      b = seq_of_key_rank(a, a.order_seqs, b, reinterpret_cast<long long*>(s_k[0]), &s_pick);
+      xb = gridDim.x - 1 - blockIdx.x;
+    }
+    int r1 = a.query_start[b + 1];
+    r0 = a.query_start[b];
+    r1 = min(r1, a.T);
+    r0 = min(max(r0, 0), r1);
+    L = r1 - r0;
+    if (xb * kPos >= L) return;
+    c = a.ctx[b];
+    const int cap = a.MB * kBlockSize;
+    c = c < 0 ? 0 : (c > cap ? cap : c);
+  }
+  const int p0 = xb * kPos;
+
   // Keys this work-group needs: the prefix and new tokens up to its last position.
   const int pend = min(L, p0 + kPos);
   const int nkeys = c + pend;
-  const int ntiles = (nkeys + kTile - 1) / kTile;
+  if (nch == 1) ntiles = (nkeys + kTile - 1) / kTile;
 
   // ---- query operands and per-row state ----
   // Column group cg of this wave: rows 16 CG w + 16cg + (0..15); lane column r16.  The
@@ -315,12 +600,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   const size_t bstride = (size_t)a.Hkv * hstride;
   const int32_t* btrow = a.bt + (size_t)b * a.MB;
   const int cmax = c > 0 ? c - 1 : 0;
+  // Tile t of the loop is tile tb + t of the row block.
   auto fetch_block = [&](int t) {  // block id of this thread's row of tile t (any if not prefix)
-    return btrow[min(t * kTile + lrow, cmax) / kBlockSize];
+    return btrow[min((tb + t) * kTile + lrow, cmax) / kBlockSize];
   };
   // Row lrow of tile t: source element offset in the cache (pre) or the new tokens.
   auto row_source = [&](int t, int blk, bool& pre, bool& ok) -> size_t {
-    const int key = t * kTile + lrow;
+    const int key = (tb + t) * kTile + lrow;
     pre = key < c && (unsigned)blk < (unsigned)a.NB;
     const bool fresh = key >= c && key < nkeys;
     ok = pre || fresh;
@@ -488,7 +774,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // Softmax of tile t: row max (masked keys become -inf on diagonal tiles, where S then
   // holds scaled logits), the rescale of O when a row max grows past the slack, and P.
   auto softmax = [&](int t) {
-    const int kbase = t * kTile;
+    const int kbase = (tb + t) * kTile;
     const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
     float bm[CG];
     bool grow = false;
@@ -531,12 +817,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         }
       }
     }
-    // m_ref is finite here: key 0 is visible to every row and lies in tile 0.
+    // m_ref is finite here except in a chunk of the planned schedule: key 0 is visible to
+    // every row and lies in tile 0.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
     const f16x2 ones2 = {(_Float16)1.f, (_Float16)1.f};  // one-part row sums: p0 + p1 + sum
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      const float nm = -m_ref[cg];
+      // A chunk of the planned schedule that starts inside the causal part can hold no
+      // visible key for some rows yet: p = 0 for them until one appears.
+      const float nm = (kSched == 2 && m_ref[cg] == kNegInf) ? 0.f : -m_ref[cg];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float p[8];
@@ -635,6 +924,33 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  // ---- a chunk of a cut row block: its partial state, for prefill_merge_kernel ----
+  // O unnormalised (relative to the row's running max), in register order, so that every
+  // store and the merge's loads are 16 bytes per lane and contiguous over a wave.
+  if (kSched == 2 && nch > 1) {
+    const size_t wb = (size_t)slot * 8 + w;
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+#pragma unroll
+      for (int jd = 0; jd < JD; ++jd)
+        *reinterpret_cast<f32x4*>(a.part_o + (((wb * CG + cg) * JD + jd) * 64 + lane) * 4) =
+            O[cg][jd];
+      float* pm = a.part_m + (wb * CG + cg) * 16;
+      float* pl = a.part_l + (wb * CG + cg) * 16;
+      if (kg == 0) pm[r16] = m_ref[cg];  // row r16's running max (base 2)
+      if constexpr (kSumMfma) {
+        if (r16 == 0) {  // Lacc[cg][i]: the sum of row 4kg + i, in every column lane
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pl[4 * kg + i] = Lacc[cg][i];
+        }
+      } else {
+        const float lrow = sum_over_groups(lsum[cg]);
+        if (kg == 0) pl[r16] = lrow;
+      }
+    }
+    return;
+  }
+
   // ---- normalise and store: lane (r16, kg) holds rows 4kg+i, head-dim 16 jd + r16 ----
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
@@ -658,47 +974,177 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 }
 
-template <int DT, int D, bool kOrder, bool kPrec>
+// Sum of per_xb(x) over position blocks x in [lo, npb) (every wave the same result).
+template <typename F>
+__device__ __forceinline__ int plan_sum(int npb, int lo, F per_xb) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int base = lo; base < npb; base += 64) {
+    const int x = base + lane;
+    int v = x < npb ? per_xb(x) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    acc += v;
+  }
+  return acc;
+}
+
+// Phase 2 of a cut row block: its chunks' (row max m_k, row sum l_k, unnormalised O_k),
+// folded in chunk order: out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k with M the
+// largest m_k (base 2).  Work-group m takes the m-th cut row block of the plan (cut row
+// blocks by sequence rank, then position block last first, then KV head); its threads
+// read the partial states in the layout the chunks wrote them (lane (r16, kg) of wave w
+// holds rows 16 CG w + 16 cg + 4 kg + i, head-dim columns 16 jd + r16).
+template <int DT, int D, int G>
+__global__ void __launch_bounds__(kThreads) prefill_merge_kernel(const PrefillArgs a) {
+  constexpr bool kBF = DT == PA_BF16;
+  using Sh = Shape<D>;
+  constexpr int CG = Sh::CG, JD = Sh::JD;
+  constexpr int kPos = Sh::ROWS / G;
+  __shared__ int s_tab[kPrefillPlanWords];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int S = a.order_seqs;
+  for (int i = tid; i < 8 + kRecWords * (S + 1); i += kThreads) s_tab[i] = a.plan[i];
+  __syncthreads();
+  const int m = blockIdx.x;
+  if (m >= s_tab[3]) return;
+  const int C = s_tab[0];
+  const int* rec = s_tab + 8;
+  const int* rr = rec + plan_search(rec, S, kRecCut, m) * kRecWords;
+  const int c = rr[kRecC], r0 = rr[kRecR0], L = rr[kRecL];
+  const int local = m - rr[kRecCut];
+  const int H = a.Hkv;
+  const int npb = (min(L, a.max_query_len) + kPos - 1) / kPos;
+  const int xb = npb - 1 - local / H;
+  const int g = local % H;
+  auto chunks = [&](int x) { return (plan_tiles(c, L, x, kPos) + C - 1) / C; };
+  const int nch = chunks(xb);
+  const int slot0 = rr[kRecSplit] + H * plan_sum(npb, xb + 1, chunks) + g * nch;
+  const int p0 = xb * kPos;
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    auto stat = [&](const float* base, int k) {  // rows 4kg .. 4kg+3 of chunk k
+      return *reinterpret_cast<const f32x4*>(base + (((size_t)(slot0 + k) * 8 + w) * CG + cg) * 16 +
+                                             4 * kg);
+    };
+    f32x4 M = {kNegInf, kNegInf, kNegInf, kNegInf};
+    for (int k = 0; k < nch; ++k) {
+      const f32x4 mk = stat(a.part_m, k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mk[i]);
+    }
+    f32x4 den = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[JD];
+#pragma unroll
+    for (int jd = 0; jd < JD; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < nch; ++k) {
+      const f32x4 mk = stat(a.part_m, k), lk = stat(a.part_l, k);
+      f32x4 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = exp2_fast(mk[i] - M[i]);
+        den[i] += f[i] * lk[i];
+      }
+      const size_t wb = (size_t)(slot0 + k) * 8 + w;
+#pragma unroll
+      for (int jd = 0; jd < JD; ++jd) {
+        const f32x4 o =
+            *reinterpret_cast<const f32x4*>(a.part_o + (((wb * CG + cg) * JD + jd) * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[jd][i] += f[i] * o[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
+      const int pos = p0 + row / G;
+      if (pos >= L) continue;
+      const int hq = g * G + row % G;
+      const float inv = 1.f / den[i];
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+      for (int jd = 0; jd < JD; jd += 2) {
+        const uint32_t two = pack2<kBF>(acc[jd][i] * inv, acc[jd + 1][i] * inv);
+        orow[16 * jd + r16] = (uint16_t)two;
+        orow[16 * (jd + 1) + r16] = (uint16_t)(two >> 16);
+      }
+    }
+  }
+}
+
+template <int DT, int D, int kSched, bool kPrec>
 hipError_t launch_gg(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
                      hipEvent_t e1) {
   const dim3 block(kThreads);
   switch (G) {
-    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
-    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kOrder, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((prefill_kernel<DT, 1, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_kernel<DT, 2, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int DT, int D>
+hipError_t launch_merge(int G, unsigned n, const PrefillArgs& a, hipStream_t st, hipEvent_t e1) {
+  const dim3 grid(n), block(kThreads);
+  switch (G) {
+    case 1: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 1>), grid, block, 0, st, nullptr, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 2>), grid, block, 0, st, nullptr, e1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 4>), grid, block, 0, st, nullptr, e1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 8>), grid, block, 0, st, nullptr, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 16>), grid, block, 0, st, nullptr, e1, 0, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Non-planned grid (position blocks, Hkv, S): most keys first with several sequences.
 template <int DT, int D, bool kPrec>
-hipError_t launch_p(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
-                    hipEvent_t e1) {
-  if (a.order_seqs > 0) return launch_gg<DT, D, true, kPrec>(G, grid, a, st, e0, e1);
-  return launch_gg<DT, D, false, kPrec>(G, grid, a, st, e0, e1);
+hipError_t launch_grid(int G, const PrefillArgs& a, int num_seqs, int max_query_len,
+                       hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const int per = Shape<D>::ROWS / G;
+  const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
+  PrefillArgs ao = a;
+  ao.order_seqs = num_seqs >= 2 && num_seqs <= kOrderMaxSeqs ? num_seqs : 0;
+  if (ao.order_seqs > 0) return launch_gg<DT, D, 1, kPrec>(G, grid, ao, st, e0, e1);
+  return launch_gg<DT, D, 0, kPrec>(G, grid, ao, st, e0, e1);
 }
 
 template <int DT, int D>
 hipError_t launch_g(int G, const PrefillArgs& a, int num_seqs, int max_query_len,
                     hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const int per = Shape<D>::ROWS / G;
-  const dim3 grid((unsigned)((max_query_len + per - 1) / per), (unsigned)a.Hkv, (unsigned)num_seqs);
   PrefillArgs ao = a;
-  ao.order_seqs = num_seqs >= 2 && num_seqs <= kOrderMaxSeqs ? num_seqs : 0;
   ao.flag_check = 0;
-  if (a.precise) return launch_p<DT, D, true>(G, grid, ao, st, e0, e1);
-  if constexpr (DT != PA_BF16) {
-    return launch_p<DT, D, false>(G, grid, ao, st, e0, e1);
-  } else {
-    // One-part form, then the two-part recompute, which runs only if the first launch
-    // marked this call's overflow word.
-    hipError_t err = launch_p<DT, D, false>(G, grid, ao, st, e0, nullptr);
+  if (a.precise) return launch_grid<DT, D, true>(G, ao, num_seqs, max_query_len, st, e0, e1);
+  // The one-part form; for bf16 the two-part recompute launch follows and ends the call.
+  hipEvent_t last = DT == PA_BF16 ? nullptr : e1;
+  hipError_t err;
+  if (a.plan) {
+    ao.order_seqs = num_seqs;
+    const int per = Shape<D>::ROWS / G;
+    hipExtLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(512), 0, st, e0, nullptr, 0, ao,
+                          num_seqs, per);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = launch_gg<DT, D, 2, false>(G, dim3((unsigned)a.item_bound), ao, st, nullptr,
+                                     a.merge_bound > 0 ? nullptr : last);
     if (err != hipSuccess) return err;
-    ao.flag_check = 1;
-    return launch_p<DT, D, true>(G, grid, ao, st, nullptr, e1);
+    if (a.merge_bound > 0 &&
+        (err = launch_merge<DT, D>(G, (unsigned)a.merge_bound, ao, st, last)) != hipSuccess)
+      return err;
+  } else {
+    err = launch_grid<DT, D, false>(G, ao, num_seqs, max_query_len, st, e0, last);
+    if (err != hipSuccess) return err;
   }
+  if constexpr (DT == PA_BF16) {
+    // Runs only if the first launch marked this call's overflow word.
+    ao.flag_check = 1;
+    return launch_grid<DT, D, true>(G, ao, num_seqs, max_query_len, st, nullptr, e1);
+  }
+  return hipSuccess;
 }
 
 // Overflow words of the one-part bf16 form: call e (a number the host draws from a
@@ -740,6 +1186,42 @@ hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch) {
   if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
   *epoch = e;
   return hipSuccess;
+}
+
+size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a) {
+  a.item_bound = a.slot_bound = a.merge_bound = 0;
+  if (a.precise || a.chunk == 0 || num_seqs < 1 || num_seqs > kOrderMaxSeqs) return 0;
+  if ((head_dim != 128 && head_dim != 256) || group < 1) return 0;
+  const long long rows = prefill_rows(head_dim);
+  const long long kpos = rows / group;
+  const long long S = num_seqs, T = a.T, maxq = a.max_query_len;
+  // Row blocks (position blocks of every sequence, times KV heads): sum_b ceil(L_b / kpos)
+  // with sum_b L_b <= T and every L_b counted up to max_query_len.
+  const long long R =
+      std::min((T + kpos - 1) / kpos + S, S * ((maxq + kpos - 1) / kpos)) * a.Hkv;
+  const long long tmax = ((long long)a.MB * kBlockSize + maxq + kTile - 1) / kTile;
+  const long long cmin = a.chunk > 0 ? a.chunk : kPrefillAutoMinChunk;
+  const long long per_rb = (tmax + cmin - 1) / cmin;  // chunks of one row block, at most
+  const long long N = std::max(a.ncu, 1);
+  // Automatic chunks: W / C <= 3N, so items <= 3N + R, chunks of cut row blocks <= 6N,
+  // cut row blocks <= 3N.  A plan beyond these is dropped on the device for the uncut one.
+  long long slots = per_rb > 1 ? R * per_rb : 0, merges = per_rb > 1 ? R : 0;
+  if (a.chunk < 0) {
+    slots = std::min(slots, 6 * N);
+    merges = std::min(merges, 3 * N);
+  }
+  constexpr long long kMaxSlots = 4096;  // about 0.5 GB of partial states
+  slots = std::min(slots, kMaxSlots);
+  merges = std::min(merges, slots / 2);
+  long long items = R + slots;
+  if (a.chunk < 0) items = std::min(items, 3 * N + R);
+  if (items > (1ll << 30)) return 0;
+  a.item_bound = (int32_t)items;
+  a.slot_bound = (int32_t)slots;
+  a.merge_bound = (int32_t)merges;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(sizeof(int32_t) * kPrefillPlanWords) + al((size_t)slots * rows * head_dim * 4) +
+         2 * al((size_t)slots * rows * 4);
 }
 
 hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs& args,

@@ -464,3 +464,17 @@ def test_prefill_mode_knob():
         assert B.pa_get_prefill_mode() == 0
     finally:
         B.pa_set_prefill_mode(old)
+
+
+def test_prefill_split_knob():
+    old = B.pa_get_prefill_split()
+    try:
+        for v in (0, 4, 16, 1 << 20, -1):
+            B.pa_set_prefill_split(v)
+            assert B.pa_get_prefill_split() == v
+        for bad in (-2, 1, 2, 3, (1 << 20) + 1):
+            with pytest.raises(B.PaError):
+                B.pa_set_prefill_split(bad)
+        assert B.pa_get_prefill_split() == -1
+    finally:
+        B.pa_set_prefill_split(old)

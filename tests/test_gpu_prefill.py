@@ -87,11 +87,21 @@ def test_pf_batch_mixed():
 
 
 def test_pf_batch_mixed_rows_equal_single_sequence_runs():
-    """With several sequences the work-groups take sequences most keys first (the longest
-    prefix plus chunk first) and position blocks last first; every sequence's rows must be
-    bitwise those of a prefill of that sequence alone (one sequence: grid order)."""
+    """Without the planned schedule (pa_set_prefill_split(0)) the work-groups take
+    sequences most keys first (the longest prefix plus chunk first) and position blocks
+    last first; every sequence's rows must be bitwise those of a prefill of that sequence
+    alone (one sequence: grid order)."""
     w = wl.prefill_config(2)
     dev = upload(w)
+    old = B.pa_get_prefill_split()
+    B.pa_set_prefill_split(0)
+    try:
+        _rows_equal_single(w, dev)
+    finally:
+        B.pa_set_prefill_split(old)
+
+
+def _rows_equal_single(w, dev):
     batch = run(w, dev)
     qs = np.asarray(w.query_start)
     for b in range(len(w.context_lens)):
