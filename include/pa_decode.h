@@ -457,12 +457,13 @@ int32_t pa_get_prefill_mode(void);
  * attends to its keys in 64-key tiles, t of them.  -1 (default): a plan kernel reads the
  * context and chunk lengths on the device, cuts every row block of more than C tiles
  * into ceil(t / C) chunks (C = max(16, ceil(W / 3N)) for W tiles in the call and N
- * compute units), and the prefill kernel takes the items longest first (chunks, then
- * whole row blocks); a merge kernel folds each cut row block's chunks with the
- * log-sum-exp rule (the same statistics as decode's Phase 2, over key ranges instead of
- * partitions).  k in 4 .. 2^20: chunks of at most k tiles, the same items otherwise
- * (results then do not depend on the rest of the batch).  0: no plan: one work-group per
- * row block in a (position block, KV head, sequence) grid, sequences most keys first.
+ * compute units), and lists the items (chunks and whole row blocks, per KV head) largest
+ * first; the prefill kernel takes them in that order, and the last chunk of a row block
+ * to finish folds its chunks with the log-sum-exp rule (the same statistics as decode's
+ * Phase 2, over key ranges instead of partitions).  k in 4 .. 2^20: chunks of at most k
+ * tiles, the same otherwise (results then do not depend on the rest of the batch).  0:
+ * no plan: one work-group per row block in a (position block, KV head, sequence) grid,
+ * sequences most keys first.
  * The plan and the chunks' partial states use the library-owned workspace (as
  * pa_decode's: grown on demand, kept per device; calls that overlap on one device from
  * different streams race).  Returns PA_ERR_UNSUPPORTED for another value. */

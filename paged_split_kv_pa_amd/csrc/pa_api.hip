@@ -689,12 +689,13 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
     if (bytes > 0) {
       void* base = nullptr;
       if ((st = owned_workspace(bytes, hs, &base)) != PA_OK) return st;
+      a.counters = static_cast<uint32_t*>(base);  // zero between launches
       char* ws = static_cast<char*>(base) + pa::kFusedCounterBytes;
       const size_t rows = (size_t)pa::prefill_rows(d->head_dim);
       const size_t o_bytes = align256((size_t)a.slot_bound * rows * d->head_dim * 4);
       const size_t s_bytes = align256((size_t)a.slot_bound * rows * 4);
       a.plan = reinterpret_cast<int32_t*>(ws);
-      a.part_o = reinterpret_cast<float*>(ws + align256(sizeof(int32_t) * pa::kPrefillPlanWords));
+      a.part_o = reinterpret_cast<float*>(ws + pa::prefill_plan_words_bytes(a.item_bound));
       a.part_m = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_o) + o_bytes);
       a.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_m) + s_bytes);
     }

@@ -160,22 +160,31 @@ struct PrefillArgs {
   uint32_t epoch = 0;
   int32_t flag_check = 0;
   // Planned schedule (see prefill_plan_kernel; one-part form, 1..kOrderMaxSeqs sequences):
-  // the plan table and the partial states of split row blocks in a workspace, the bounds
-  // the host sized them for, the compute-unit count and the chunk setting (-1 automatic,
-  // >= kPrefillMinChunk a fixed chunk length in 64-key tiles; 0: no planned schedule).
+  // the plan table and the partial states of split row blocks in a workspace (below
+  // 2 GiB: addressed by 32-bit offsets from plan), the bounds the host sized them for,
+  // the compute-unit count and the chunk setting (-1 automatic, >= kPrefillMinChunk a
+  // fixed chunk length in 64-key tiles; 0: no planned schedule).
   int32_t* plan = nullptr;
+  // Arrival counters of cut row blocks (word 16 m for the m-th one): zero before the
+  // launch and again after it (the library-owned workspace's zeroed counter region).
+  uint32_t* counters = nullptr;
   float* part_o = nullptr;   // [slot][8 waves][CG][JD][64 lanes] f32x4
   float* part_m = nullptr;   // [slot][8 waves][CG][16 rows]
   float* part_l = nullptr;   // [slot][8 waves][CG][16 rows]
   int32_t max_query_len = 0;
   int32_t ncu = 0;
   int32_t chunk = 0;
-  int32_t item_bound = 0, slot_bound = 0, merge_bound = 0;
+  int32_t item_bound = 0, slot_bound = 0;
+  int32_t merge_bound = 0;   // cut row blocks (each with an arrival counter)
 };
 constexpr int kPrefillFlagSlots = 1024;
 constexpr int kPrefillMinChunk = 4;       // tiles; a chunk then spans at least 2 tiles
 constexpr int kPrefillAutoMinChunk = 16;  // tiles; the automatic chunk length's floor
-constexpr int kPrefillPlanWords = 8 + 8 * (kOrderMaxSeqs + 1);  // header + records
+// Bytes of the plan (a header of 8 words and 16 words per item), 256-byte aligned.
+constexpr size_t prefill_plan_words_bytes(long long items) {
+  return ((size_t)4 * (8 + 16 * (size_t)items) + 255) & ~(size_t)255;
+}
+constexpr int kPrefillCounterStride = 16;  // words: one 64-byte line per counter
 // Query rows (position, head) of one prefill work-group.
 constexpr int prefill_rows(int head_dim) { return head_dim == 128 ? 256 : 128; }
 // Grid (ceil(max_query_len / positions per work-group), Hkv, S); head_dim 128 or 256,

@@ -202,30 +202,37 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
 
 // ---- planned schedule ----------------------------------------------------------------
 // A row block is the work of the non-planned grid's work-group: positions [p0, p0 + kPos)
-// of one sequence and one KV head, over keys [0, c + min(L, p0 + kPos)) in 64-key tiles.
+// of one sequence and one KV head, over keys [0, c + min(L, p0 + kPos)) in t 64-key tiles.
 // Work-groups start in grid order and one runs per compute unit, so a launch whose row
 // blocks differ in length (a long prefix next to short ones, or a few row blocks over a
 // long prefix) ends on its longest row blocks alone.  The planned schedule cuts every
-// row block of more than C tiles into ceil(t / C) chunks of consecutive tiles (C =
+// row block of more than C tiles into nch = ceil(t / C) chunks of consecutive tiles (C =
 // max(16, ceil(W / 3N)) for W tiles in the launch over N compute units: about three
-// chunks' worth of work per unit), and hands out items longest first: work-group j
-// takes item j of the list
-//   the chunks of the cut row blocks, then the uncut row blocks,
-// each part by sequence in most-keys-first order, then position block last first, then
-// KV head (then chunk).  A chunk writes its (row max, row sum, unnormalised output) to a
-// slot of the workspace (slot = its item index); prefill_merge_kernel folds the chunks
-// of each cut row block with the log-sum-exp rule, in chunk order.  Within a sequence t
-// grows with the position block, so the cut row blocks are those from position block
-// xs on.  A chunk spans at least two tiles; a row that sees no key of a chunk (possible
-// when the chunk starts inside the causal part) leaves (-inf, 0, 0), which the merge
-// weighs by 0.
+// chunks' worth of work per unit) and lists the items (a chunk, or a whole row block, of
+// one KV head) largest first; work-group j takes entry j of the list, so the dispatcher
+// hands out the work longest-processing-time first.
 //
-// Plan table (int32, in the workspace): header {C, split items S1, items, cut row
-// blocks}, then per rank r (S + 1 records of 8 words; record S holds the totals):
-// {sequence, c, r0, L, xs, split prefix, uncut prefix, cut-row-block prefix}, prefixes
-// counted over KV heads.
-constexpr int kRecWords = 8;
-enum { kRecSeq = 0, kRecC, kRecR0, kRecL, kRecXs, kRecSplit, kRecUncut, kRecCut };
+// prefill_plan_kernel writes the list: a stable counting sort by item size (tiles, capped
+// at kSizeKeys - 1) from largest to smallest, over row blocks in a fixed order (sequences
+// most keys first, then position block last first), each row block's items by KV head,
+// then chunk.  A chunk writes its (row max, row sum, unnormalised output) to a slot of the
+// workspace (the chunks of one row block and head in consecutive slots); the last chunk
+// of a row block and head to finish folds them all with the log-sum-exp rule, in chunk
+// order (see the end of prefill_kernel), with one arrival counter per row block and head.
+// A row that sees no key of a chunk (when the chunk starts inside the causal part) leaves
+// (-inf, 0, 0), which the fold weighs by 0.
+//
+// Workspace: header {C, chunk items with slots, items, cut (row block, head) pairs}, then
+// one entry of kItemWords int32 per item.
+constexpr int kItemWords = 16;
+enum { kItB = 0, kItG, kItXb, kItK, kItNch, kItSlot, kItCut, kItC, kItR0, kItL, kItTb, kItNt };
+constexpr int kSizeKeys = 4096;
+constexpr int kScDev = 16;  // cache-policy bits of a device-scope access (sc1)
+
+// Buffer resource over the prefill workspace (offsets below 2 GiB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
 
 __device__ __forceinline__ int plan_tiles(int c, int L, int xb, int kpos) {
   return (c + min(L, (xb + 1) * kpos) + kTile - 1) / kTile;
@@ -255,59 +262,18 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return off + incl - v;
 }
 
-// Largest r in [0, n) with rec[r][field] <= key (rec[0][field] == 0 <= key).
-__device__ __forceinline__ int plan_search(const int* rec, int n, int field, int key) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (rec[mid * kRecWords + field] <= key) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Position block of the `local`-th cut item (or cut row block) of a sequence, walking
-// position blocks from npb - 1 down to xs, each worth per_xb(xb) items; returns xb and
-// sets *before to the items of the position blocks after it.  Every wave computes the
-// same result (no LDS, no barrier).
-template <typename F>
-__device__ __forceinline__ int plan_walk(int npb, int xs, int local, F per_xb, int* before) {
-  const int lane = threadIdx.x & 63;
-  int acc = 0;
-  for (int base = npb - 1; base >= xs; base -= 64) {
-    const int xb = base - lane;
-    const int v = xb >= xs ? per_xb(xb) : 0;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    const unsigned long long hit = __ballot(acc + incl > local);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      *before = acc + __shfl(incl - v, l);
-      return base - l;
-    }
-    acc += __shfl(incl, 63);
-  }
-  *before = acc;  // not reached for a local index inside the sequence's items
-  return xs;
-}
-
-// One work-group of 512 threads; S <= kOrderMaxSeqs sequences.
+// One work-group of 512 threads; S <= kOrderMaxSeqs sequences; kpos query positions per
+// row block.
 __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, int S, int kpos) {
   __shared__ int s_c[kOrderMaxSeqs], s_r0[kOrderMaxSeqs], s_L[kOrderMaxSeqs];
-  __shared__ int s_npb[kOrderMaxSeqs + 1], s_xs[kOrderMaxSeqs];
-  __shared__ int s_order[kOrderMaxSeqs];
-  __shared__ unsigned long long s_w[kOrderMaxSeqs];
-  __shared__ int s_nsp[kOrderMaxSeqs], s_ncut[kOrderMaxSeqs];
+  __shared__ int s_npb[kOrderMaxSeqs], s_order[kOrderMaxSeqs], s_rbpre[kOrderMaxSeqs + 1];
+  __shared__ int s_bucket[kSizeKeys];  // items per size key, then the key's next position
+  __shared__ int s_key[512], s_cnt[512];
   __shared__ int s_tmp[8];
   __shared__ unsigned long long s_wsum;
   const int tid = threadIdx.x;
   const int cap = a.MB * kBlockSize;
-  const int maxq = a.max_query_len;
-  int my_npb = 0;
+  const int H = a.Hkv;
   if (tid < S) {
     int r1 = a.query_start[tid + 1], r0 = a.query_start[tid];
     r1 = min(r1, a.T);
@@ -317,69 +283,12 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     s_c[tid] = c;
     s_r0[tid] = r0;
     s_L[tid] = r1 - r0;
-    my_npb = (min(r1 - r0, maxq) + kpos - 1) / kpos;
-    s_xs[tid] = my_npb;
-    s_w[tid] = 0;
-    s_nsp[tid] = 0;
-    s_ncut[tid] = 0;
+    s_npb[tid] = (min(r1 - r0, a.max_query_len) + kpos - 1) / kpos;
   }
+  for (int k = tid; k < kSizeKeys; k += blockDim.x) s_bucket[k] = 0;
   if (tid == 0) s_wsum = 0;
-  int nrb = 0;
-  const int pre = block_exclusive_scan(tid < S ? my_npb : 0, s_tmp, &nrb);
-  if (tid < S) s_npb[tid] = pre;  // exclusive prefix of row blocks per sequence
-  if (tid == 0) s_npb[S] = nrb;
   __syncthreads();
-  auto seq_of = [&](int p) {  // sequence of flat row block p (s_npb is non-decreasing)
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_npb[mid] <= p) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-  // Tiles per sequence (one KV head), then W.
-  for (int p = tid; p < nrb; p += blockDim.x) {
-    const int b = seq_of(p);
-    atomicAdd(&s_w[b], (unsigned long long)plan_tiles(s_c[b], s_L[b], p - s_npb[b], kpos));
-  }
-  __syncthreads();
-  if (tid < S) atomicAdd(&s_wsum, s_w[tid]);
-  __syncthreads();
-  const unsigned long long W = s_wsum * (unsigned long long)a.Hkv;
-  const unsigned long long per = 3ull * (unsigned long long)max(a.ncu, 1);
-  long long C = a.chunk > 0 ? a.chunk
-                            : max((long long)kPrefillAutoMinChunk, (long long)((W + per - 1) / per));
-  // Cut counts, first cut position block.
-  for (int p = tid; p < nrb; p += blockDim.x) {
-    const int b = seq_of(p), xb = p - s_npb[b];
-    const long long t = plan_tiles(s_c[b], s_L[b], xb, kpos);
-    const long long n = (t + C - 1) / C;
-    if (n > 1) {
-      atomicAdd(&s_nsp[b], (int)n);
-      atomicAdd(&s_ncut[b], 1);
-      atomicMin(&s_xs[b], xb);
-    }
-  }
-  __syncthreads();
-  // Totals; a plan beyond the sizes the host provided for (not expected) is dropped for
-  // the uncut schedule, which always fits.
-  int tsplit = 0, tuncut = 0, tcut = 0;
-  (void)block_exclusive_scan(tid < S ? s_nsp[tid] : 0, s_tmp, &tsplit);
-  (void)block_exclusive_scan(tid < S ? s_xs[tid] : 0, s_tmp, &tuncut);
-  (void)block_exclusive_scan(tid < S ? s_ncut[tid] : 0, s_tmp, &tcut);
-  const long long H = a.Hkv;
-  if (H * tsplit > a.slot_bound || H * (tsplit + tuncut) > a.item_bound ||
-      H * tcut > a.merge_bound) {
-    C = 0x7fffffff;
-    if (tid < S) {
-      s_nsp[tid] = 0;
-      s_ncut[tid] = 0;
-      s_xs[tid] = my_npb;
-    }
-    __syncthreads();
-  }
-  // Most keys first (prefix plus new tokens; ties by index), as the non-planned order.
+  // Sequences most keys first (prefix plus new tokens; ties by index).
   if (tid < S) {
     const long long kc = (long long)s_c[tid] + s_L[tid];
     int rank = 0;
@@ -390,34 +299,131 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     s_order[rank] = tid;
   }
   __syncthreads();
-  const int b = tid < S ? s_order[tid] : 0;
-  int nsplit = 0, nuncut = 0, ncut = 0;
-  const int psplit = block_exclusive_scan(tid < S ? a.Hkv * s_nsp[b] : 0, s_tmp, &nsplit);
-  const int puncut = block_exclusive_scan(tid < S ? a.Hkv * s_xs[b] : 0, s_tmp, &nuncut);
-  const int pcut = block_exclusive_scan(tid < S ? a.Hkv * s_ncut[b] : 0, s_tmp, &ncut);
-  int* rec = a.plan + 8;
-  if (tid <= S) {
-    int* r = rec + tid * kRecWords;
-    if (tid < S) {
-      r[kRecSeq] = b;
-      r[kRecC] = s_c[b];
-      r[kRecR0] = s_r0[b];
-      r[kRecL] = s_L[b];
-      r[kRecXs] = s_xs[b];
-      r[kRecSplit] = psplit;
-      r[kRecUncut] = puncut;
-      r[kRecCut] = pcut;
-    } else {
-      r[kRecSeq] = r[kRecC] = r[kRecR0] = r[kRecL] = r[kRecXs] = 0;
-      r[kRecSplit] = nsplit;
-      r[kRecUncut] = nuncut;
-      r[kRecCut] = ncut;
+  int nrb = 0;
+  const int pre = block_exclusive_scan(tid < S ? s_npb[s_order[tid]] : 0, s_tmp, &nrb);
+  if (tid < S) s_rbpre[tid] = pre;  // by rank
+  // Row block p (fixed order): rank r with s_rbpre[r] <= p, position block last first.
+  auto row_block = [&](int p, int& b, int& xb) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_rbpre[mid] <= p) lo = mid;
+      else hi = mid - 1;
     }
+    b = s_order[lo];
+    xb = s_npb[b] - 1 - (p - s_rbpre[lo]);
+  };
+  __syncthreads();
+  for (int p = tid; p < nrb; p += blockDim.x) {
+    int b, xb;
+    row_block(p, b, xb);
+    atomicAdd(&s_wsum, (unsigned long long)plan_tiles(s_c[b], s_L[b], xb, kpos));
+  }
+  __syncthreads();
+  const unsigned long long W = s_wsum * (unsigned long long)H;
+  const unsigned long long per = 3ull * (unsigned long long)max(a.ncu, 1);
+  long long C = a.chunk > 0 ? a.chunk
+                            : max((long long)kPrefillAutoMinChunk, (long long)((W + per - 1) / per));
+  // Pass 1 (twice at most): items per size key and the totals.  A plan beyond the sizes
+  // the host provided for (not expected) falls back to whole row blocks, which fit.
+  int nitems = 0, nslots = 0, ncut = 0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    int li = 0, ls = 0, lc = 0;
+    for (int p = tid; p < nrb; p += blockDim.x) {
+      int b, xb;
+      row_block(p, b, xb);
+      const long long t = plan_tiles(s_c[b], s_L[b], xb, kpos);
+      const int nch = (int)((t + C - 1) / C);
+      const int key = (int)min((t + nch - 1) / nch, (long long)kSizeKeys - 1);
+      atomicAdd(&s_bucket[key], H * nch);
+      li += H * nch;
+      ls += nch > 1 ? H * nch : 0;
+      lc += nch > 1 ? H : 0;
+    }
+    (void)block_exclusive_scan(li, s_tmp, &nitems);
+    (void)block_exclusive_scan(ls, s_tmp, &nslots);
+    (void)block_exclusive_scan(lc, s_tmp, &ncut);
+    if (nitems <= a.item_bound && nslots <= a.slot_bound && ncut <= a.merge_bound) break;
+    C = 0x7fffffff;
+    for (int k = tid; k < kSizeKeys; k += blockDim.x) s_bucket[k] = 0;
+    __syncthreads();
+  }
+  // Whole row blocks always fit for query_start as the interface requires (non-decreasing,
+  // so the chunks add up to at most T); otherwise nothing is listed and nothing written.
+  if (nitems > a.item_bound || nslots > a.slot_bound || ncut > a.merge_bound) {
+    if (tid == 0) {
+      a.plan[0] = (int)C;
+      a.plan[1] = a.plan[2] = a.plan[3] = 0;
+    }
+    return;
+  }
+  // Positions: keys from the largest down (thread t owns keys [8t, 8t + 8)).
+  {
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kSizeKeys / 512; ++i) sum += s_bucket[kSizeKeys - 1 - (tid * 8 + i)];
+    int tot = 0;
+    int off = block_exclusive_scan(sum, s_tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < kSizeKeys / 512; ++i) {
+      const int k = kSizeKeys - 1 - (tid * 8 + i);
+      const int n = s_bucket[k];
+      s_bucket[k] = off;
+      off += n;
+    }
+  }
+  __syncthreads();
+  // Pass 2, in rounds of 512 row blocks in the fixed order: a row block's items go after
+  // those of earlier row blocks with the same key (stable), then slots and counters.
+  int* items = a.plan + 8;
+  int slot_base = 0, cut_base = 0;
+  for (int p0 = 0; p0 < nrb; p0 += blockDim.x) {
+    const int p = p0 + tid;
+    int b = 0, xb = 0, nch = 0, key = -1;
+    long long t = 0;
+    if (p < nrb) {
+      row_block(p, b, xb);
+      t = plan_tiles(s_c[b], s_L[b], xb, kpos);
+      nch = (int)((t + C - 1) / C);
+      key = (int)min((t + nch - 1) / nch, (long long)kSizeKeys - 1);
+    }
+    s_key[tid] = key;
+    s_cnt[tid] = H * nch;
+    int nsl = 0, ncu = 0;
+    const int sl = block_exclusive_scan(nch > 1 ? H * nch : 0, s_tmp, &nsl);  // has barriers
+    const int cu = block_exclusive_scan(nch > 1 ? H : 0, s_tmp, &ncu);
+    int pos = 0;
+    if (p < nrb) {
+      pos = s_bucket[key];
+      for (int q = 0; q < tid; ++q) pos += s_key[q] == key ? s_cnt[q] : 0;
+      for (int g = 0; g < H; ++g)
+        for (int k = 0; k < nch; ++k) {
+          int* e = items + (size_t)(pos + g * nch + k) * kItemWords;
+          const int tb = (int)(k * t / nch);
+          e[kItB] = b;
+          e[kItG] = g;
+          e[kItXb] = xb;
+          e[kItK] = k;
+          e[kItNch] = nch;
+          e[kItSlot] = nch > 1 ? slot_base + sl + g * nch + k : 0;
+          e[kItCut] = nch > 1 ? cut_base + cu + g : 0;
+          e[kItC] = s_c[b];
+          e[kItR0] = s_r0[b];
+          e[kItL] = s_L[b];
+          e[kItTb] = tb;
+          e[kItNt] = (int)((k + 1) * t / nch) - tb;
+        }
+    }
+    __syncthreads();  // every thread has read s_bucket and the round's keys
+    if (p < nrb) atomicAdd(&s_bucket[key], H * nch);
+    slot_base += nsl;
+    cut_base += ncu;
+    __syncthreads();
   }
   if (tid == 0) {
     a.plan[0] = (int)C;
-    a.plan[1] = nsplit;
-    a.plan[2] = nsplit + nuncut;
+    a.plan[1] = nslots;
+    a.plan[2] = nitems;
     a.plan[3] = ncut;
   }
 }
@@ -461,56 +467,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   int g, b, xb, r0, L, c;
   // Tiles [tb, tb + ntiles) of the row block (all of them unless it is cut), chunk k of
   // nch; a cut row block's chunk writes its partial state to slot `slot`.
-  int tb = 0, ntiles, nch = 1, slot = 0;
+  int tb = 0, ntiles, nch = 1, slot = 0, kchunk = 0, cut_ord = 0;
   if constexpr (kSched == 2) {
-    // The plan table lives in the second V tile buffer until the first barrier of the
-    // tile loop (that buffer is first written after it).
-    int* s_tab = reinterpret_cast<int*>(s_v[1]);
-    const int S = a.order_seqs;
-    for (int i = tid; i < 8 + kRecWords * (S + 1); i += kThreads) s_tab[i] = a.plan[i];
-    __syncthreads();
+    // Entry j of the plan's item list (scalar loads: the address is uniform).
     const int j = blockIdx.x;
-    const int C = s_tab[0], S1 = s_tab[1];
-    if (j >= s_tab[2]) return;
-    const int* rec = s_tab + 8;
-    const bool cut = j < S1;
-    const int key = cut ? j : j - S1;
-    const int r = plan_search(rec, S, cut ? kRecSplit : kRecUncut, key);
-    const int* rr = rec + r * kRecWords;
-    b = rr[kRecSeq];
-    c = rr[kRecC];
-    r0 = rr[kRecR0];
-    L = rr[kRecL];
-    const int xs = rr[kRecXs];
-    const int local = key - rr[cut ? kRecSplit : kRecUncut];
-    if (cut) {
-      const int npb = (min(L, a.max_query_len) + kPos - 1) / kPos;
-      const int H = a.Hkv;
-      int before = 0;
-      xb = plan_walk(npb, xs, local,
-                     [&](int x) { return H * ((plan_tiles(c, L, x, kPos) + C - 1) / C); },
-                     &before);
-      nch = (plan_tiles(c, L, xb, kPos) + C - 1) / C;
-      const int rem = local - before;
-      g = rem / nch;
-      const int k = rem - g * nch;
-      const int t_all = plan_tiles(c, L, xb, kPos);
-      tb = k * t_all / nch;
-      ntiles = (k + 1) * t_all / nch - tb;
-      slot = j;
-    } else {
-      xb = xs - 1 - local / a.Hkv;
-      g = local % a.Hkv;
-    }
-    b = __builtin_amdgcn_readfirstlane(b);
-    g = __builtin_amdgcn_readfirstlane(g);
-    xb = __builtin_amdgcn_readfirstlane(xb);
-    c = __builtin_amdgcn_readfirstlane(c);
-    L = __builtin_amdgcn_readfirstlane(L);
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    tb = __builtin_amdgcn_readfirstlane(tb);
-    nch = __builtin_amdgcn_readfirstlane(nch);
-    if (nch > 1) ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+    const int* e = a.plan + 8 + (size_t)j * kItemWords;
+    if (j >= a.plan[2]) return;
+    b = e[kItB];
+    g = e[kItG];
+    xb = e[kItXb];
+    kchunk = e[kItK];
+    nch = e[kItNch];
+    slot = e[kItSlot];
+    cut_ord = e[kItCut];
+    c = e[kItC];
+    r0 = e[kItR0];
+    L = e[kItL];
+    tb = e[kItTb];
+    ntiles = e[kItNt];
   } else {
     g = blockIdx.y;
     b = blockIdx.z;
@@ -536,7 +510,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // Keys this work-group needs: the prefix and new tokens up to its last position.
   const int pend = min(L, p0 + kPos);
   const int nkeys = c + pend;
-  if (nch == 1) ntiles = (nkeys + kTile - 1) / kTile;
+  if (kSched != 2) ntiles = (nkeys + kTile - 1) / kTile;
 
   // ---- query operands and per-row state ----
   // Column group cg of this wave: rows 16 CG w + 16cg + (0..15); lane column r16.  The
@@ -924,28 +898,106 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- a chunk of a cut row block: its partial state, for prefill_merge_kernel ----
+  // ---- a chunk of a cut row block: its partial state; the last chunk to finish folds ----
   // O unnormalised (relative to the row's running max), in register order, so that every
-  // store and the merge's loads are 16 bytes per lane and contiguous over a wave.
+  // store and load is 16 bytes per lane and contiguous over a wave.  The stores are
+  // device-scope (they reach the memory side, where a work-group on another XCD reads
+  // them); each wave waits for its own, then one thread counts the chunk in the row
+  // block's arrival counter.  The work-group that completes the count resets it and
+  // folds all chunks from memory, in chunk order (so the result does not depend on which
+  // chunk came last): out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k, M = max m_k.
   if (kSched == 2 && nch > 1) {
-    const size_t wb = (size_t)slot * 8 + w;
+    const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.plan);
+    const char* const wsb = reinterpret_cast<const char*>(a.plan);
+    auto off = [&](const float* p) { return (int)(reinterpret_cast<const char*>(p) - wsb); };
+    auto o_at = [&](int sl, int cg, int jd) {
+      return a.part_o + ((((size_t)sl * 8 + w) * CG + cg) * JD + jd) * 256 + lane * 4;
+    };
+    auto st_at = [&](float* base, int sl, int cg) {
+      return base + (((size_t)sl * 8 + w) * CG + cg) * 16;
+    };
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
 #pragma unroll
       for (int jd = 0; jd < JD; ++jd)
-        *reinterpret_cast<f32x4*>(a.part_o + (((wb * CG + cg) * JD + jd) * 64 + lane) * 4) =
-            O[cg][jd];
-      float* pm = a.part_m + (wb * CG + cg) * 16;
-      float* pl = a.part_l + (wb * CG + cg) * 16;
-      if (kg == 0) pm[r16] = m_ref[cg];  // row r16's running max (base 2)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O[cg][jd]), rs,
+                                               off(o_at(slot, cg, jd)), 0, kScDev);
+      if (kg == 0)  // row r16's running max (base 2)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref[cg]), rs,
+                                              off(st_at(a.part_m, slot, cg) + r16), 0, kScDev);
       if constexpr (kSumMfma) {
         if (r16 == 0) {  // Lacc[cg][i]: the sum of row 4kg + i, in every column lane
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pl[4 * kg + i] = Lacc[cg][i];
+          for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(Lacc[cg][i]), rs, off(st_at(a.part_l, slot, cg) + 4 * kg + i), 0,
+                kScDev);
         }
       } else {
         const float lrow = sum_over_groups(lsum[cg]);
-        if (kg == 0) pl[r16] = lrow;
+        if (kg == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lrow), rs,
+                                                off(st_at(a.part_l, slot, cg) + r16), 0, kScDev);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores performed
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t* const cnt = a.counters + (size_t)kPrefillCounterStride * cut_ord;
+      const unsigned prev =
+          __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev + 1 == (unsigned)nch;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_pick = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_pick) return;
+    const int slot0 = slot - kchunk;
+    auto ld4 = [&](const float* p) {
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(p), 0, kScDev));
+    };
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      f32x4 M = {kNegInf, kNegInf, kNegInf, kNegInf};
+      for (int k = 0; k < nch; ++k) {
+        const f32x4 mk = ld4(st_at(a.part_m, slot0 + k, cg) + 4 * kg);  // rows 4kg .. 4kg+3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mk[i]);
+      }
+      f32x4 den = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[JD];
+#pragma unroll
+      for (int jd = 0; jd < JD; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < nch; ++k) {
+        const f32x4 mk = ld4(st_at(a.part_m, slot0 + k, cg) + 4 * kg);
+        const f32x4 lk = ld4(st_at(a.part_l, slot0 + k, cg) + 4 * kg);
+        f32x4 f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = exp2_fast(mk[i] - M[i]);  // 0 for a row that saw no key of chunk k
+          den[i] += f[i] * lk[i];
+        }
+#pragma unroll
+        for (int jd = 0; jd < JD; ++jd) {
+          const f32x4 o = ld4(o_at(slot0 + k, cg, jd));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[jd][i] += f[i] * o[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
+        const int pos = p0 + row / G;
+        if (pos >= L) continue;
+        const int hq = g * G + row % G;
+        const float inv = 1.f / den[i];
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+        for (int jd = 0; jd < JD; jd += 2) {
+          const uint32_t two = pack2<kBF>(acc[jd][i] * inv, acc[jd + 1][i] * inv);
+          orow[16 * jd + r16] = (uint16_t)two;
+          orow[16 * (jd + 1) + r16] = (uint16_t)(two >> 16);
+        }
       }
     }
     return;
@@ -974,105 +1026,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   }
 }
 
-// Sum of per_xb(x) over position blocks x in [lo, npb) (every wave the same result).
-template <typename F>
-__device__ __forceinline__ int plan_sum(int npb, int lo, F per_xb) {
-  const int lane = threadIdx.x & 63;
-  int acc = 0;
-  for (int base = lo; base < npb; base += 64) {
-    const int x = base + lane;
-    int v = x < npb ? per_xb(x) : 0;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-    acc += v;
-  }
-  return acc;
-}
-
-// Phase 2 of a cut row block: its chunks' (row max m_k, row sum l_k, unnormalised O_k),
-// folded in chunk order: out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k with M the
-// largest m_k (base 2).  Work-group m takes the m-th cut row block of the plan (cut row
-// blocks by sequence rank, then position block last first, then KV head); its threads
-// read the partial states in the layout the chunks wrote them (lane (r16, kg) of wave w
-// holds rows 16 CG w + 16 cg + 4 kg + i, head-dim columns 16 jd + r16).
-template <int DT, int D, int G>
-__global__ void __launch_bounds__(kThreads) prefill_merge_kernel(const PrefillArgs a) {
-  constexpr bool kBF = DT == PA_BF16;
-  using Sh = Shape<D>;
-  constexpr int CG = Sh::CG, JD = Sh::JD;
-  constexpr int kPos = Sh::ROWS / G;
-  __shared__ int s_tab[kPrefillPlanWords];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int S = a.order_seqs;
-  for (int i = tid; i < 8 + kRecWords * (S + 1); i += kThreads) s_tab[i] = a.plan[i];
-  __syncthreads();
-  const int m = blockIdx.x;
-  if (m >= s_tab[3]) return;
-  const int C = s_tab[0];
-  const int* rec = s_tab + 8;
-  const int* rr = rec + plan_search(rec, S, kRecCut, m) * kRecWords;
-  const int c = rr[kRecC], r0 = rr[kRecR0], L = rr[kRecL];
-  const int local = m - rr[kRecCut];
-  const int H = a.Hkv;
-  const int npb = (min(L, a.max_query_len) + kPos - 1) / kPos;
-  const int xb = npb - 1 - local / H;
-  const int g = local % H;
-  auto chunks = [&](int x) { return (plan_tiles(c, L, x, kPos) + C - 1) / C; };
-  const int nch = chunks(xb);
-  const int slot0 = rr[kRecSplit] + H * plan_sum(npb, xb + 1, chunks) + g * nch;
-  const int p0 = xb * kPos;
-#pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    auto stat = [&](const float* base, int k) {  // rows 4kg .. 4kg+3 of chunk k
-      return *reinterpret_cast<const f32x4*>(base + (((size_t)(slot0 + k) * 8 + w) * CG + cg) * 16 +
-                                             4 * kg);
-    };
-    f32x4 M = {kNegInf, kNegInf, kNegInf, kNegInf};
-    for (int k = 0; k < nch; ++k) {
-      const f32x4 mk = stat(a.part_m, k);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mk[i]);
-    }
-    f32x4 den = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[JD];
-#pragma unroll
-    for (int jd = 0; jd < JD; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < nch; ++k) {
-      const f32x4 mk = stat(a.part_m, k), lk = stat(a.part_l, k);
-      f32x4 f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = exp2_fast(mk[i] - M[i]);
-        den[i] += f[i] * lk[i];
-      }
-      const size_t wb = (size_t)(slot0 + k) * 8 + w;
-#pragma unroll
-      for (int jd = 0; jd < JD; ++jd) {
-        const f32x4 o =
-            *reinterpret_cast<const f32x4*>(a.part_o + (((wb * CG + cg) * JD + jd) * 64 + lane) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[jd][i] += f[i] * o[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * CG * w + 16 * cg + 4 * kg + i;
-      const int pos = p0 + row / G;
-      if (pos >= L) continue;
-      const int hq = g * G + row % G;
-      const float inv = 1.f / den[i];
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * a.Hq + hq) * D;
-#pragma unroll
-      for (int jd = 0; jd < JD; jd += 2) {
-        const uint32_t two = pack2<kBF>(acc[jd][i] * inv, acc[jd + 1][i] * inv);
-        orow[16 * jd + r16] = (uint16_t)two;
-        orow[16 * (jd + 1) + r16] = (uint16_t)(two >> 16);
-      }
-    }
-  }
-}
-
 template <int DT, int D, int kSched, bool kPrec>
 hipError_t launch_gg(int G, const dim3& grid, const PrefillArgs& a, hipStream_t st, hipEvent_t e0,
                      hipEvent_t e1) {
@@ -1083,20 +1036,6 @@ hipError_t launch_gg(int G, const dim3& grid, const PrefillArgs& a, hipStream_t 
     case 4: hipExtLaunchKernelGGL((prefill_kernel<DT, 4, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
     case 8: hipExtLaunchKernelGGL((prefill_kernel<DT, 8, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
     case 16: hipExtLaunchKernelGGL((prefill_kernel<DT, 16, D, kSched, kPrec>), grid, block, 0, st, e0, e1, 0, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int DT, int D>
-hipError_t launch_merge(int G, unsigned n, const PrefillArgs& a, hipStream_t st, hipEvent_t e1) {
-  const dim3 grid(n), block(kThreads);
-  switch (G) {
-    case 1: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 1>), grid, block, 0, st, nullptr, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 2>), grid, block, 0, st, nullptr, e1, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 4>), grid, block, 0, st, nullptr, e1, 0, a); break;
-    case 8: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 8>), grid, block, 0, st, nullptr, e1, 0, a); break;
-    case 16: hipExtLaunchKernelGGL((prefill_merge_kernel<DT, D, 16>), grid, block, 0, st, nullptr, e1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1129,12 +1068,8 @@ hipError_t launch_g(int G, const PrefillArgs& a, int num_seqs, int max_query_len
     hipExtLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(512), 0, st, e0, nullptr, 0, ao,
                           num_seqs, per);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    err = launch_gg<DT, D, 2, false>(G, dim3((unsigned)a.item_bound), ao, st, nullptr,
-                                     a.merge_bound > 0 ? nullptr : last);
+    err = launch_gg<DT, D, 2, false>(G, dim3((unsigned)a.item_bound), ao, st, nullptr, last);
     if (err != hipSuccess) return err;
-    if (a.merge_bound > 0 &&
-        (err = launch_merge<DT, D>(G, (unsigned)a.merge_bound, ao, st, last)) != hipSuccess)
-      return err;
   } else {
     err = launch_grid<DT, D, false>(G, ao, num_seqs, max_query_len, st, e0, last);
     if (err != hipSuccess) return err;
@@ -1211,8 +1146,10 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
     merges = std::min(merges, 3 * N);
   }
   constexpr long long kMaxSlots = 4096;  // about 0.5 GB of partial states
+  static_assert(kItemWords == 16, "item entries of 64 bytes");
+  constexpr long long kMaxCut = (long long)(kFusedCounterBytes / (4 * kPrefillCounterStride));
   slots = std::min(slots, kMaxSlots);
-  merges = std::min(merges, slots / 2);
+  merges = std::min(std::min(merges, slots / 2), kMaxCut);  // one arrival counter each
   long long items = R + slots;
   if (a.chunk < 0) items = std::min(items, 3 * N + R);
   if (items > (1ll << 30)) return 0;
@@ -1220,7 +1157,7 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
   a.slot_bound = (int32_t)slots;
   a.merge_bound = (int32_t)merges;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(sizeof(int32_t) * kPrefillPlanWords) + al((size_t)slots * rows * head_dim * 4) +
+  return prefill_plan_words_bytes(a.item_bound) + al((size_t)slots * rows * head_dim * 4) +
          2 * al((size_t)slots * rows * 4);
 }
 
