@@ -212,10 +212,11 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
 // one KV head) largest first; work-group j takes entry j of the list, so the dispatcher
 // hands out the work longest-processing-time first.
 //
-// prefill_plan_kernel writes the list: a stable counting sort by item size (tiles, capped
-// at kSizeKeys - 1) from largest to smallest, over row blocks in a fixed order (sequences
-// most keys first, then position block last first), each row block's items by KV head,
-// then chunk.  A chunk writes its (row max, row sum, unnormalised output) to a slot of the
+// prefill_plan_kernel writes the list: a counting sort by item size (tiles, capped at
+// kSizeKeys - 1) from largest to smallest; each row block reserves its items' places in
+// its size bucket with one LDS atomic (so the order among equal sizes varies from run to
+// run; no result depends on it: an item's work, slot and fold order follow from its row
+// block, head and chunk alone), its items by KV head, then chunk.  A chunk writes its (row max, row sum, unnormalised output) to a slot of the
 // workspace (the chunks of one row block and head in consecutive slots); the last chunk
 // of a row block and head to finish folds them all with the log-sum-exp rule, in chunk
 // order (see the end of prefill_kernel), with one arrival counter per row block and head.
@@ -268,7 +269,6 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   __shared__ int s_c[kOrderMaxSeqs], s_r0[kOrderMaxSeqs], s_L[kOrderMaxSeqs];
   __shared__ int s_npb[kOrderMaxSeqs], s_order[kOrderMaxSeqs], s_rbpre[kOrderMaxSeqs + 1];
   __shared__ int s_bucket[kSizeKeys];  // items per size key, then the key's next position
-  __shared__ int s_key[512], s_cnt[512];
   __shared__ int s_tmp[8];
   __shared__ unsigned long long s_wsum;
   const int tid = threadIdx.x;
@@ -373,8 +373,9 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     }
   }
   __syncthreads();
-  // Pass 2, in rounds of 512 row blocks in the fixed order: a row block's items go after
-  // those of earlier row blocks with the same key (stable), then slots and counters.
+  // Pass 2, in rounds of 512 row blocks in the fixed order (sequences most keys first,
+  // position blocks last first): places in the size buckets, then slots and counters,
+  // which follow the fixed order.
   int* items = a.plan + 8;
   int slot_base = 0, cut_base = 0;
   for (int p0 = 0; p0 < nrb; p0 += blockDim.x) {
@@ -387,38 +388,26 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
       nch = (int)((t + C - 1) / C);
       key = (int)min((t + nch - 1) / nch, (long long)kSizeKeys - 1);
     }
-    s_key[tid] = key;
-    s_cnt[tid] = H * nch;
     int nsl = 0, ncu = 0;
     const int sl = block_exclusive_scan(nch > 1 ? H * nch : 0, s_tmp, &nsl);  // has barriers
     const int cu = block_exclusive_scan(nch > 1 ? H : 0, s_tmp, &ncu);
-    int pos = 0;
     if (p < nrb) {
-      pos = s_bucket[key];
-      for (int q = 0; q < tid; ++q) pos += s_key[q] == key ? s_cnt[q] : 0;
+      const int pos = atomicAdd(&s_bucket[key], H * nch);
       for (int g = 0; g < H; ++g)
         for (int k = 0; k < nch; ++k) {
-          int* e = items + (size_t)(pos + g * nch + k) * kItemWords;
+          // Words kItB .. kItNt as three 16-byte stores.
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          i32x4* e = reinterpret_cast<i32x4*>(items + (size_t)(pos + g * nch + k) * kItemWords);
           const int tb = (int)(k * t / nch);
-          e[kItB] = b;
-          e[kItG] = g;
-          e[kItXb] = xb;
-          e[kItK] = k;
-          e[kItNch] = nch;
-          e[kItSlot] = nch > 1 ? slot_base + sl + g * nch + k : 0;
-          e[kItCut] = nch > 1 ? cut_base + cu + g : 0;
-          e[kItC] = s_c[b];
-          e[kItR0] = s_r0[b];
-          e[kItL] = s_L[b];
-          e[kItTb] = tb;
-          e[kItNt] = (int)((k + 1) * t / nch) - tb;
+          static_assert(kItB == 0 && kItNch == 4 && kItTb == 10 && kItNt == 11, "entry layout");
+          e[0] = i32x4{b, g, xb, k};
+          e[1] = i32x4{nch, nch > 1 ? slot_base + sl + g * nch + k : 0, nch > 1 ? cut_base + cu + g : 0,
+                       s_c[b]};
+          e[2] = i32x4{s_r0[b], s_L[b], tb, (int)((k + 1) * t / nch) - tb};
         }
     }
-    __syncthreads();  // every thread has read s_bucket and the round's keys
-    if (p < nrb) atomicAdd(&s_bucket[key], H * nch);
     slot_base += nsl;
     cut_base += ncu;
-    __syncthreads();
   }
   if (tid == 0) {
     a.plan[0] = (int)C;
