@@ -463,7 +463,8 @@ int32_t pa_get_prefill_mode(void);
  * Phase 2, over key ranges instead of partitions).  k in 4 .. 2^20: chunks of at most k
  * tiles, the same otherwise (results then do not depend on the rest of the batch).  0:
  * no plan: one work-group per row block in a (position block, KV head, sequence) grid,
- * sequences most keys first.
+ * sequences most keys first; -1 takes this grid too when no row block can exceed 16
+ * tiles (prefix plus chunk bound by the table width and max_query_len: 1024 keys).
  * The plan and the chunks' partial states use the library-owned workspace (as
  * pa_decode's: grown on demand, kept per device; calls that overlap on one device from
  * different streams race).  Returns PA_ERR_UNSUPPORTED for another value. */

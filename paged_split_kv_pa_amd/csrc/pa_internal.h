@@ -160,7 +160,7 @@ struct PrefillArgs {
   uint32_t epoch = 0;
   int32_t flag_check = 0;
   // Planned schedule (see prefill_plan_kernel; one-part form, 1..kOrderMaxSeqs sequences):
-  // the plan table and the partial states of split row blocks in a workspace (below
+  // the item list and the partial states of cut row blocks in a workspace (below
   // 2 GiB: addressed by 32-bit offsets from plan), the bounds the host sized them for,
   // the compute-unit count and the chunk setting (-1 automatic, >= kPrefillMinChunk a
   // fixed chunk length in 64-key tiles; 0: no planned schedule).
@@ -175,7 +175,7 @@ struct PrefillArgs {
   int32_t ncu = 0;
   int32_t chunk = 0;
   int32_t item_bound = 0, slot_bound = 0;
-  int32_t merge_bound = 0;   // cut row blocks (each with an arrival counter)
+  int32_t cut_bound = 0;     // cut (row block, KV head) pairs, each with an arrival counter
 };
 constexpr int kPrefillFlagSlots = 1024;
 constexpr int kPrefillMinChunk = 4;       // tiles; a chunk then spans at least 2 tiles
@@ -196,7 +196,7 @@ hipError_t launch_prefill(int dtype, int group, int head_dim, const PrefillArgs&
 // and a fresh call number (never 0) for the one-part bf16 prefill.
 hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch);
 // Whether a prefill launch takes the planned schedule, and the workspace bytes it needs
-// (0 if it does not); fills the bounds in a (item_bound, slot_bound, merge_bound).
+// (0 if it does not); fills the bounds in a (item_bound, slot_bound, cut_bound).
 size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a);
 
 }  // namespace pa

@@ -343,14 +343,14 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     (void)block_exclusive_scan(li, s_tmp, &nitems);
     (void)block_exclusive_scan(ls, s_tmp, &nslots);
     (void)block_exclusive_scan(lc, s_tmp, &ncut);
-    if (nitems <= a.item_bound && nslots <= a.slot_bound && ncut <= a.merge_bound) break;
+    if (nitems <= a.item_bound && nslots <= a.slot_bound && ncut <= a.cut_bound) break;
     C = 0x7fffffff;
     for (int k = tid; k < kSizeKeys; k += blockDim.x) s_bucket[k] = 0;
     __syncthreads();
   }
   // Whole row blocks always fit for query_start as the interface requires (non-decreasing,
   // so the chunks add up to at most T); otherwise nothing is listed and nothing written.
-  if (nitems > a.item_bound || nslots > a.slot_bound || ncut > a.merge_bound) {
+  if (nitems > a.item_bound || nslots > a.slot_bound || ncut > a.cut_bound) {
     if (tid == 0) {
       a.plan[0] = (int)C;
       a.plan[1] = a.plan[2] = a.plan[3] = 0;
@@ -1113,7 +1113,7 @@ hipError_t prefill_overflow_flags(uint32_t** words, uint32_t* epoch) {
 }
 
 size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a) {
-  a.item_bound = a.slot_bound = a.merge_bound = 0;
+  a.item_bound = a.slot_bound = a.cut_bound = 0;
   if (a.precise || a.chunk == 0 || num_seqs < 1 || num_seqs > kOrderMaxSeqs) return 0;
   if ((head_dim != 128 && head_dim != 256) || group < 1) return 0;
   const long long rows = prefill_rows(head_dim);
@@ -1126,6 +1126,9 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
   const long long tmax = ((long long)a.MB * kBlockSize + maxq + kTile - 1) / kTile;
   const long long cmin = a.chunk > 0 ? a.chunk : kPrefillAutoMinChunk;
   const long long per_rb = (tmax + cmin - 1) / cmin;  // chunks of one row block, at most
+  // Automatic chunks and no row block long enough to be cut (at most 16 tiles, a small
+  // call): the grid schedule, without the plan kernel's latency.
+  if (a.chunk < 0 && per_rb <= 1) return 0;
   const long long N = std::max(a.ncu, 1);
   // Automatic chunks: W / C <= 3N, so items <= 3N + R, chunks of cut row blocks <= 6N,
   // cut row blocks <= 3N.  A plan beyond these is dropped on the device for the uncut one.
@@ -1144,7 +1147,7 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
   if (items > (1ll << 30)) return 0;
   a.item_bound = (int32_t)items;
   a.slot_bound = (int32_t)slots;
-  a.merge_bound = (int32_t)merges;
+  a.cut_bound = (int32_t)merges;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return prefill_plan_words_bytes(a.item_bound) + al((size_t)slots * rows * head_dim * 4) +
          2 * al((size_t)slots * rows * 4);
