@@ -431,6 +431,25 @@ pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const 
                                 const int32_t* context_lens, const int32_t* query_start,
                                 float scale, void* stream, void* start_event, void* stop_event);
 
+/* pa_prefill with a caller-provided workspace instead of the library's (for calls that
+ * overlap on one device from different streams: each needs a workspace of its own).
+ * workspace_bytes must be at least pa_prefill_workspace_bytes(dims) under the settings
+ * in force at the call (0: workspace may be NULL); the workspace is 256-byte aligned, and
+ * its first 320 KiB (a counter region) must be zero before its first use; every call
+ * leaves them zero.  PA_ERR_WORKSPACE if it is NULL or too small where one is needed,
+ * PA_ERR_ALIGN if it is misaligned. */
+pa_status_t pa_prefill_ex(const pa_prefill_dims_t* dims, void* out, const void* q,
+                          const void* k_new, const void* v_new, const void* k_cache,
+                          const void* v_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes a prefill with these dims needs under the current settings (the planned
+ * schedule's item list, partial states and counter region; 0 when the call takes the grid
+ * schedule), or a negative pa_status_t.  Reads the device's compute-unit count (PA_ERR_HIP
+ * without a device).  The library's own prefill workspace is separate from pa_decode's,
+ * so a decode and a prefill call may overlap on two streams. */
+int64_t pa_prefill_workspace_bytes(const pa_prefill_dims_t* dims);
+
 /* How pa_prefill feeds the probabilities P to the PV products (the matrix cores take
  * 16-bit operands).  Process-wide; env PA_PREFILL_MODE sets the initial value.
  *   0 (default): P as one fp16 value (11 significant bits) and V as fp16; bf16 V is
@@ -465,9 +484,10 @@ int32_t pa_get_prefill_mode(void);
  * no plan: one work-group per row block in a (position block, KV head, sequence) grid,
  * sequences most keys first; -1 takes this grid too when no row block can exceed 16
  * tiles (prefix plus chunk bound by the table width and max_query_len: 1024 keys).
- * The plan and the chunks' partial states use the library-owned workspace (as
- * pa_decode's: grown on demand, kept per device; calls that overlap on one device from
- * different streams race).  Returns PA_ERR_UNSUPPORTED for another value. */
+ * The plan and the chunks' partial states use the library-owned prefill workspace
+ * (grown on demand, kept per device, about 0.2 GB at most at 256 compute units; prefill
+ * calls that overlap on one device from different streams race: give them pa_prefill_ex
+ * workspaces) or pa_prefill_ex's.  Returns PA_ERR_UNSUPPORTED for another value. */
 pa_status_t pa_set_prefill_split(int32_t chunk_tiles);
 int32_t pa_get_prefill_split(void);
 

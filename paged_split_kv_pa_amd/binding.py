@@ -101,6 +101,9 @@ SIGNATURES = {
                           ctypes.c_float, _P]),
     "pa_prefill_profiled": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, ctypes.c_float, _P, _P, _P]),
+    "pa_prefill_ex": (_I32, [ctypes.POINTER(PaPrefillDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "pa_prefill_workspace_bytes": (_I64, [ctypes.POINTER(PaPrefillDims)]),
 }
 
 LAYOUT_FIELDS = 9
@@ -430,9 +433,21 @@ def prefill_dims_of(q, k_new, k_cache, block_tables, context_lens, max_query_len
                          _dtype_code(q), int(max_query_len))
 
 
+def pa_prefill_workspace_bytes(q, k_new, k_cache, block_tables, context_lens, max_query_len=0):
+    """Bytes of the workspace pa_prefill_ex needs for these tensors (0: none)."""
+    d = prefill_dims_of(q, k_new, k_cache, block_tables, context_lens, max_query_len)
+    r = int(lib().pa_prefill_workspace_bytes(ctypes.byref(d)))
+    if r < 0:
+        _check(r)
+    return r
+
+
 def pa_prefill(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, query_start,
-               scale, max_query_len=0, stream=None, start_event=None, stop_event=None):
-    """Paged prefix-prefill attention (include/pa_decode.h, pa_prefill); all device tensors."""
+               scale, max_query_len=0, stream=None, start_event=None, stop_event=None,
+               workspace=None):
+    """Paged prefix-prefill attention (include/pa_decode.h, pa_prefill); all device tensors.
+    With `workspace` (a uint8 device tensor, see pa_prefill_workspace_bytes) the call goes
+    through pa_prefill_ex."""
     d = prefill_dims_of(q, k_new, k_cache, block_tables, context_lens, max_query_len)
     for name, t in (("out", out), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
                     ("v_cache", v_cache)):
@@ -450,7 +465,13 @@ def pa_prefill(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_len
             _ptr(block_tables, "block_tables", torch.int32),
             _ptr(context_lens, "context_lens", torch.int32),
             _ptr(query_start, "query_start", torch.int32))
-    if start_event is None and stop_event is None:
+    if workspace is not None:
+        if start_event is not None or stop_event is not None:
+            raise PaError(-9, "timestamps are taken with the library's workspace only")
+        _check(lib().pa_prefill_ex(ctypes.byref(d), *ptrs, float(scale),
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   _stream(stream)))
+    elif start_event is None and stop_event is None:
         _check(lib().pa_prefill(ctypes.byref(d), *ptrs, float(scale), _stream(stream)))
     else:
         _check(lib().pa_prefill_profiled(ctypes.byref(d), *ptrs, float(scale), _stream(stream),

@@ -447,28 +447,32 @@ pa_status_t run_reduce(const pa_dims_t* dims, const Plan& pl, void* out, const i
   return hip_status(pa::launch_reduce(dims->dtype, pl.D, r, pl.S, st), "phase-2 reduce launch");
 }
 
-// Library-owned workspace, grow-only, one per device.
+// Library-owned workspaces, grow-only, one per device for decode and one for prefill
+// (so that a decode and a prefill call overlapping on two streams do not share memory).
 constexpr int kMaxDevices = 64;
+enum WsKind { kWsDecode = 0, kWsPrefill = 1 };
 std::mutex g_ws_mutex;
-void* g_ws_ptr[kMaxDevices] = {};
-size_t g_ws_size[kMaxDevices] = {};
+void* g_ws_ptr[2][kMaxDevices] = {};
+size_t g_ws_size[2][kMaxDevices] = {};
 
-// Library-managed workspaces (pa_decode's and pa_decode_noalloc's) start with the
-// counters of a single-launch V2 (pa::kFusedCounterBytes, zero between launches); the
-// partials follow.  The counters are zeroed (by a fill kernel on the caller's stream)
-// whenever the memory is new.
-pa_status_t owned_workspace(size_t bytes, hipStream_t stream, void** out) {
+// Library-managed workspaces (pa_decode's, pa_decode_noalloc's and pa_prefill's) start
+// with a counter region (pa::kFusedCounterBytes, zero between launches: the single-launch
+// V2's counters and flags, the prefill chunks' arrival counters); the rest follows.  The
+// counters are zeroed (by a fill kernel on the caller's stream) whenever the memory is new.
+pa_status_t owned_workspace(WsKind kind, size_t bytes, hipStream_t stream, void** out) {
   bytes += pa::kFusedCounterBytes;
   int dev = 0;
   pa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
   if (st != PA_OK) return st;
   if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_INTERNAL, "device id %d out of range", dev);
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if (g_ws_size[dev] < bytes) {
-    if (g_ws_ptr[dev]) {
-      st = hip_status(hipFree(g_ws_ptr[dev]), "hipFree(workspace)");
-      g_ws_ptr[dev] = nullptr;
-      g_ws_size[dev] = 0;
+  void*& ptr = g_ws_ptr[kind][dev];
+  size_t& size = g_ws_size[kind][dev];
+  if (size < bytes) {
+    if (ptr) {
+      st = hip_status(hipFree(ptr), "hipFree(workspace)");
+      ptr = nullptr;
+      size = 0;
       if (st != PA_OK) return st;
     }
     void* p = nullptr;
@@ -481,10 +485,10 @@ pa_status_t owned_workspace(size_t bytes, hipStream_t stream, void** out) {
       (void)hipFree(p);
       return st;
     }
-    g_ws_ptr[dev] = p;
-    g_ws_size[dev] = bytes;
+    ptr = p;
+    size = bytes;
   }
-  *out = g_ws_ptr[dev];
+  *out = ptr;
   return ok();
 }
 
@@ -585,7 +589,7 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   }
   if (wsm == Ws::kOwned) {
     void* base = nullptr;
-    if ((st = owned_workspace(pl.ws_bytes, hs, &base)) != PA_OK) return st;
+    if ((st = owned_workspace(kWsDecode, pl.ws_bytes, hs, &base)) != PA_OK) return st;
     counters = static_cast<uint32_t*>(base);
     workspace = static_cast<char*>(base) + pa::kFusedCounterBytes;
   } else if (wsm == Ws::kCaller) {
@@ -614,10 +618,8 @@ pa_status_t decode_impl(const pa_dims_t* dims, void* out, const void* q, const v
   return run_reduce(dims, pl, out, ctx, workspace, hs, sp);
 }
 
-pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, const void* kn,
-                         const void* vn, const void* kc, const void* vc, const int32_t* bt,
-                         const int32_t* ctx, const int32_t* qs, float scale, void* stream,
-                         hipEvent_t e0, hipEvent_t e1) {
+// Validation of prefill dims (no pointer is looked at); *G receives Hq / Hkv.
+pa_status_t check_prefill_dims(const pa_prefill_dims_t* d, int* G_out) {
   if (!d) return fail(PA_ERR_NULL, "dims is NULL");
   if (d->dtype != PA_F32 && d->dtype != PA_F16 && d->dtype != PA_BF16)
     return fail(PA_ERR_DTYPE, "unknown dtype %d", d->dtype);
@@ -642,6 +644,7 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   if (d->block_size != pa::kBlockSize)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (16)", d->block_size);
   const int G = d->num_q_heads / d->num_kv_heads;
+  *G_out = G;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not built (1, 2, 4, 8, 16)", G);
   if ((int64_t)d->max_blocks_per_seq * pa::kBlockSize > (int64_t)0x3fffffff)
@@ -649,8 +652,60 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
                 d->max_blocks_per_seq);
   if (d->num_kv_heads > 65535 || d->num_seqs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "num_kv_heads and num_seqs must be <= 65535 (grid limits)");
-  pa_status_t st = check_scale(scale);
+  return ok();
+}
+
+// The planned schedule's needs for these dims under the current settings: fills the plan
+// fields of a (bounds, compute units, settings) and *bytes with the workspace bytes the
+// call needs, counter region included (0: the grid schedule, no workspace).
+pa_status_t prefill_plan(const pa_prefill_dims_t* d, int G, pa::PrefillArgs& a, size_t* bytes) {
+  *bytes = 0;
+  a.T = d->num_tokens;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.NB = d->num_blocks;
+  a.MB = d->max_blocks_per_seq;
+  a.precise = prefill_mode_setting();
+  a.max_query_len = d->max_query_len > 0 ? d->max_query_len : d->num_tokens;
+  a.chunk = prefill_split_setting();
+  if (a.precise || a.chunk == 0 || d->num_seqs <= 0 || d->num_seqs > pa::kOrderMaxSeqs ||
+      d->num_tokens <= 0)
+    return ok();
+  // A call that cannot take the planned schedule is told apart without the device.
+  a.ncu = 1;
+  if (pa::prefill_plan_bytes(d->head_dim, G, d->num_seqs, a) == 0) return ok();
+  int ncu = 0;
+  pa_status_t st = compute_units(&ncu);
   if (st != PA_OK) return st;
+  a.ncu = ncu;
+  const size_t b = pa::prefill_plan_bytes(d->head_dim, G, d->num_seqs, a);
+  if (b > 0) *bytes = b + pa::kFusedCounterBytes;
+  return ok();
+}
+
+// Plan, partial-state and counter pointers of a prefill workspace at base (256-byte
+// aligned, bytes from prefill_plan).
+void prefill_carve(pa::PrefillArgs& a, int head_dim, void* base) {
+  a.counters = static_cast<uint32_t*>(base);  // zero between launches
+  char* ws = static_cast<char*>(base) + pa::kFusedCounterBytes;
+  const size_t rows = (size_t)pa::prefill_rows(head_dim);
+  const size_t o_bytes = align256((size_t)a.slot_bound * rows * head_dim * 4);
+  const size_t s_bytes = align256((size_t)a.slot_bound * rows * 4);
+  a.plan = reinterpret_cast<int32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(ws + pa::prefill_plan_words_bytes(a.item_bound));
+  a.part_m = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_o) + o_bytes);
+  a.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_m) + s_bytes);
+}
+
+pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, const void* kn,
+                         const void* vn, const void* kc, const void* vc, const int32_t* bt,
+                         const int32_t* ctx, const int32_t* qs, float scale, Ws wsm,
+                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t e0,
+                         hipEvent_t e1) {
+  int G = 0;
+  pa_status_t st = check_prefill_dims(d, &G);
+  if (st != PA_OK) return st;
+  if ((st = check_scale(scale)) != PA_OK) return st;
   if (d->num_seqs == 0 || d->num_tokens == 0) return ok();
   if (!out || !q || !kn || !vn || !kc || !vc || !bt || !ctx || !qs)
     return fail(PA_ERR_NULL, "a tensor pointer is NULL");
@@ -660,7 +715,6 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   if ((reinterpret_cast<uintptr_t>(bt) | reinterpret_cast<uintptr_t>(ctx) |
        reinterpret_cast<uintptr_t>(qs)) & 3u)
     return fail(PA_ERR_ALIGN, "block_tables, context_lens and query_start must be 4-byte aligned");
-  const int maxq = d->max_query_len > 0 ? d->max_query_len : d->num_tokens;
   pa::PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -672,36 +726,28 @@ pa_status_t prefill_impl(const pa_prefill_dims_t* d, void* out, const void* q, c
   a.ctx = ctx;
   a.query_start = qs;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  a.T = d->num_tokens;
-  a.Hq = d->num_q_heads;
-  a.Hkv = d->num_kv_heads;
-  a.NB = d->num_blocks;
-  a.MB = d->max_blocks_per_seq;
-  a.precise = prefill_mode_setting();
-  a.max_query_len = maxq;
-  a.chunk = prefill_split_setting();
+  size_t bytes = 0;
+  if ((st = prefill_plan(d, G, a, &bytes)) != PA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (!a.precise && a.chunk != 0 && d->num_seqs <= pa::kOrderMaxSeqs) {
-    int ncu = 0;
-    if ((st = compute_units(&ncu)) != PA_OK) return st;
-    a.ncu = ncu;
-    const size_t bytes = pa::prefill_plan_bytes(d->head_dim, G, d->num_seqs, a);
-    if (bytes > 0) {
-      void* base = nullptr;
-      if ((st = owned_workspace(bytes, hs, &base)) != PA_OK) return st;
-      a.counters = static_cast<uint32_t*>(base);  // zero between launches
-      char* ws = static_cast<char*>(base) + pa::kFusedCounterBytes;
-      const size_t rows = (size_t)pa::prefill_rows(d->head_dim);
-      const size_t o_bytes = align256((size_t)a.slot_bound * rows * d->head_dim * 4);
-      const size_t s_bytes = align256((size_t)a.slot_bound * rows * 4);
-      a.plan = reinterpret_cast<int32_t*>(ws);
-      a.part_o = reinterpret_cast<float*>(ws + pa::prefill_plan_words_bytes(a.item_bound));
-      a.part_m = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_o) + o_bytes);
-      a.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_m) + s_bytes);
+  if (bytes > 0) {
+    void* base = nullptr;
+    if (wsm == Ws::kOwned) {
+      if ((st = owned_workspace(kWsPrefill, bytes - pa::kFusedCounterBytes, hs, &base)) != PA_OK)
+        return st;
+    } else {
+      if (!workspace)
+        return fail(PA_ERR_WORKSPACE, "workspace is NULL; this prefill needs %zu bytes", bytes);
+      if (workspace_bytes < bytes)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    workspace_bytes, bytes);
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PA_ERR_ALIGN, "the prefill workspace must be 256-byte aligned");
+      base = workspace;
     }
+    prefill_carve(a, d->head_dim, base);
   }
-  return hip_status(pa::launch_prefill(d->dtype, G, d->head_dim, a, d->num_seqs, maxq,
-                                       static_cast<hipStream_t>(stream), e0, e1),
+  return hip_status(pa::launch_prefill(d->dtype, G, d->head_dim, a, d->num_seqs, a.max_query_len,
+                                       hs, e0, e1),
                     "prefill launch");
 }
 
@@ -867,11 +913,13 @@ void pa_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int cur = -1;
   bool have_cur = hipGetDevice(&cur) == hipSuccess;
-  for (int d = 0; d < kMaxDevices; ++d) {
-    if (!g_ws_ptr[d]) continue;
-    if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws_ptr[d]);
-    g_ws_ptr[d] = nullptr;
-    g_ws_size[d] = 0;
+  for (int k = 0; k < 2; ++k) {
+    for (int d = 0; d < kMaxDevices; ++d) {
+      if (!g_ws_ptr[k][d]) continue;
+      if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws_ptr[k][d]);
+      g_ws_ptr[k][d] = nullptr;
+      g_ws_size[k][d] = 0;
+    }
   }
   if (have_cur) (void)hipSetDevice(cur);
 }
@@ -938,7 +986,8 @@ pa_status_t pa_prefill(const pa_prefill_dims_t* dims, void* out, const void* q,
                        void* stream) {
   try {
     return prefill_impl(dims, out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                        context_lens, query_start, scale, stream, nullptr, nullptr);
+                        context_lens, query_start, scale, Ws::kOwned, nullptr, 0, stream, nullptr,
+                        nullptr);
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }
@@ -951,8 +1000,36 @@ pa_status_t pa_prefill_profiled(const pa_prefill_dims_t* dims, void* out, const 
                                 float scale, void* stream, void* start_event, void* stop_event) {
   try {
     return prefill_impl(dims, out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                        context_lens, query_start, scale, stream,
+                        context_lens, query_start, scale, Ws::kOwned, nullptr, 0, stream,
                         static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+pa_status_t pa_prefill_ex(const pa_prefill_dims_t* dims, void* out, const void* q,
+                          const void* k_new, const void* v_new, const void* k_cache,
+                          const void* v_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    return prefill_impl(dims, out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                        context_lens, query_start, scale, Ws::kCaller, workspace,
+                        workspace_bytes, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+int64_t pa_prefill_workspace_bytes(const pa_prefill_dims_t* dims) {
+  try {
+    int G = 0;
+    pa_status_t st = check_prefill_dims(dims, &G);
+    if (st != PA_OK) return st;
+    pa::PrefillArgs a;
+    size_t bytes = 0;
+    if ((st = prefill_plan(dims, G, a, &bytes)) != PA_OK) return st;
+    return (int64_t)bytes;
   } catch (...) {
     return fail(PA_ERR_INTERNAL, "unexpected C++ exception");
   }

@@ -478,3 +478,36 @@ def test_prefill_split_knob():
         assert B.pa_get_prefill_split() == -1
     finally:
         B.pa_set_prefill_split(old)
+
+
+def test_prefill_workspace_bytes_without_a_device():
+    """Calls that cannot take the planned schedule need no workspace, and that is decided
+    without the device; calls that can need the compute-unit count (PA_ERR_HIP here if no
+    device is visible)."""
+    lib = B.lib()
+    old_split, old_mode = B.pa_get_prefill_split(), B.pa_get_prefill_mode()
+    try:
+        small = pdims(max_blocks_per_seq=8, num_tokens=64)  # <= 16 tiles per row block
+        assert lib.pa_prefill_workspace_bytes(ctypes.byref(small)) == 0
+        big = pdims(max_blocks_per_seq=4096, num_tokens=4096)
+        r = lib.pa_prefill_workspace_bytes(ctypes.byref(big))
+        assert r == -8 or r > 320 * 1024
+        B.pa_set_prefill_split(0)
+        assert lib.pa_prefill_workspace_bytes(ctypes.byref(big)) == 0
+        B.pa_set_prefill_split(-1)
+        B.pa_set_prefill_mode(1)
+        assert lib.pa_prefill_workspace_bytes(ctypes.byref(big)) == 0
+        assert lib.pa_prefill_workspace_bytes(None) == -1
+        assert lib.pa_prefill_workspace_bytes(ctypes.byref(pdims(head_dim=64))) == -6
+    finally:
+        B.pa_set_prefill_split(old_split)
+        B.pa_set_prefill_mode(old_mode)
+
+
+def test_prefill_ex_validation_without_a_device():
+    lib = B.lib()
+    nul = [ctypes.c_void_p(0)] * 9
+    # empty calls need nothing
+    assert lib.pa_prefill_ex(ctypes.byref(pdims(num_seqs=0)), *nul, 0.1, None, 0, None) == 0
+    assert lib.pa_prefill_ex(None, *PF_FAKE, 0.1, None, 0, None) == -1
+    assert lib.pa_prefill_ex(ctypes.byref(pdims()), *PF_FAKE, float("inf"), None, 0, None) == -3

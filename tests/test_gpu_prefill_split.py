@@ -213,3 +213,73 @@ def test_bf16_beyond_fp16_in_a_cut_row_block():
     with prefill_mode(1):
         two = run(w, dev)
     assert torch.equal(got, two)
+
+
+def test_caller_workspace_matches_library_workspace():
+    """pa_prefill_ex with a zeroed workspace of pa_prefill_workspace_bytes: bitwise the
+    library-workspace result, twice in a row (the counters are left at zero); a workspace
+    one byte short is refused."""
+    w = wl.prefill_config(2)
+    dev = upload(w)
+    want = run(w, dev)
+    nbytes = B.pa_prefill_workspace_bytes(dev["q"], dev["k_new"], dev["k_cache"],
+                                          dev["block_tables"], dev["context_lens"])
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for i in range(2):
+        say(f"pa_prefill_ex call {i} ({nbytes} bytes of workspace)")
+        out = torch.empty_like(dev["q"])
+        B.pa_prefill(out, dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                     dev["block_tables"], dev["context_lens"], dev["query_start"], w.scale,
+                     workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"call {i}"
+    with pytest.raises(B.PaError) as e:
+        B.pa_prefill(torch.empty_like(dev["q"]), dev["q"], dev["k_new"], dev["v_new"],
+                     dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                     dev["query_start"], w.scale, workspace=ws[:nbytes - 1])
+    assert e.value.status == -7
+
+
+def test_decode_and_prefills_overlap_on_three_streams():
+    """A decode (library workspace) and two prefills (one on the library's prefill
+    workspace, one on a caller workspace) enqueued on three streams with no waits between
+    them: every result bitwise equal to the same call made alone."""
+    from helpers import small_workload, upload as upload_decode
+    wd = small_workload(3970, [60000, 7000], 32, 4, 128, "bf16")
+    ddev = upload_decode(wd)
+    w1 = wl.prefill_config(2)
+    w2 = wl.make_prefill_workload("overlap", 3971, context_lens=[12000, 300], query_lens=[70, 400],
+                                  num_q_heads=32, num_kv_heads=4, head_dim=128, dtype="bf16")
+    d1, d2 = upload(w1), upload(w2)
+
+    def decode(out, stream=None):
+        B.pa_decode(out, ddev["q"], ddev["k_cache"], ddev["v_cache"], ddev["block_tables"],
+                    ddev["context_lens"], wd.scale, 512, stream=stream)
+
+    alone_d = torch.empty_like(ddev["q"])
+    decode(alone_d)
+    alone_1 = run(w1, d1)
+    nbytes = B.pa_prefill_workspace_bytes(d2["q"], d2["k_new"], d2["k_cache"],
+                                          d2["block_tables"], d2["context_lens"])
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    alone_2 = torch.empty_like(d2["q"])
+    B.pa_prefill(alone_2, d2["q"], d2["k_new"], d2["v_new"], d2["k_cache"], d2["v_cache"],
+                 d2["block_tables"], d2["context_lens"], d2["query_start"], w2.scale, workspace=ws)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for rep in range(3):
+        say(f"decode + two prefills on three streams, round {rep}")
+        od, o1, o2 = torch.empty_like(alone_d), torch.empty_like(alone_1), torch.empty_like(alone_2)
+        torch.cuda.synchronize()
+        decode(od, stream=streams[0])
+        B.pa_prefill(o1, d1["q"], d1["k_new"], d1["v_new"], d1["k_cache"], d1["v_cache"],
+                     d1["block_tables"], d1["context_lens"], d1["query_start"], w1.scale,
+                     stream=streams[1])
+        B.pa_prefill(o2, d2["q"], d2["k_new"], d2["v_new"], d2["k_cache"], d2["v_cache"],
+                     d2["block_tables"], d2["context_lens"], d2["query_start"], w2.scale,
+                     stream=streams[2], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(od, alone_d), "decode"
+        assert torch.equal(o1, alone_1), "prefill on the library workspace"
+        assert torch.equal(o2, alone_2), "prefill on the caller workspace"
