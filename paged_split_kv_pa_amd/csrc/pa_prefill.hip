@@ -207,17 +207,18 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
 // blocks differ in length (a long prefix next to short ones, or a few row blocks over a
 // long prefix) ends on its longest row blocks alone.  The planned schedule cuts every
 // row block of more than C tiles into nch = ceil(t / C) chunks of consecutive tiles (C =
-// max(16, ceil(W / 3N)) for W tiles in the launch over N compute units: about three
-// chunks' worth of work per unit) and lists the items (a chunk, or a whole row block, of
-// one KV head) largest first; work-group j takes entry j of the list, so the dispatcher
-// hands out the work longest-processing-time first.
+// max(16, ceil(2W / 5N)) for W tiles in the launch over N compute units: about 2.5
+// chunks' worth of work per unit; 2N and 3N measured slower) and lists the items (a
+// chunk, or a whole row block, of one KV head) largest first; work-group j takes entry j
+// of the list, so the dispatcher hands out the work longest-processing-time first.
 //
 // prefill_plan_kernel writes the list: a counting sort by item size (tiles, capped at
 // kSizeKeys - 1) from largest to smallest; each row block reserves its items' places in
 // its size bucket with one LDS atomic (so the order among equal sizes varies from run to
 // run; no result depends on it: an item's work, slot and fold order follow from its row
-// block, head and chunk alone), its items by KV head, then chunk.  A chunk writes its (row max, row sum, unnormalised output) to a slot of the
-// workspace (the chunks of one row block and head in consecutive slots); the last chunk
+// block, head and chunk alone), its items by KV head, then chunk.  A chunk writes its
+// (row max, row sum, unnormalised output) to a slot of the workspace (the chunks of one
+// row block and head in consecutive slots); the last chunk
 // of a row block and head to finish folds them all with the log-sum-exp rule, in chunk
 // order (see the end of prefill_kernel), with one arrival counter per row block and head.
 // A row that sees no key of a chunk (when the chunk starts inside the causal part) leaves
@@ -321,9 +322,10 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   }
   __syncthreads();
   const unsigned long long W = s_wsum * (unsigned long long)H;
-  const unsigned long long per = 3ull * (unsigned long long)max(a.ncu, 1);
+  const unsigned long long per = 5ull * (unsigned long long)max(a.ncu, 1);  // C >= W / 2.5N
   long long C = a.chunk > 0 ? a.chunk
-                            : max((long long)kPrefillAutoMinChunk, (long long)((W + per - 1) / per));
+                            : max((long long)kPrefillAutoMinChunk,
+                                  (long long)((2 * W + per - 1) / per));
   // Pass 1 (twice at most): items per size key and the totals.  A plan beyond the sizes
   // the host provided for (not expected) falls back to whole row blocks, which fit.
   int nitems = 0, nslots = 0, ncut = 0;
@@ -1130,8 +1132,9 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
   // call): the grid schedule, without the plan kernel's latency.
   if (a.chunk < 0 && per_rb <= 1) return 0;
   const long long N = std::max(a.ncu, 1);
-  // Automatic chunks: W / C <= 3N, so items <= 3N + R, chunks of cut row blocks <= 6N,
-  // cut row blocks <= 3N.  A plan beyond these is dropped on the device for the uncut one.
+  // Automatic chunks: W / C <= 2.5N, so items <= 2.5N + R, chunks of cut row blocks
+  // <= 5N, cut row blocks <= 2.5N (the bounds below keep 3N and 6N).  A plan beyond these
+  // is dropped on the device for the uncut one.
   long long slots = per_rb > 1 ? R * per_rb : 0, merges = per_rb > 1 ? R : 0;
   if (a.chunk < 0) {
     slots = std::min(slots, 6 * N);
