@@ -650,6 +650,8 @@ pa_status_t check_prefill_dims(const pa_prefill_dims_t* d, int* G_out) {
   if ((int64_t)d->max_blocks_per_seq * pa::kBlockSize > (int64_t)0x3fffffff)
     return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq %d exceeds the 2^30-token limit",
                 d->max_blocks_per_seq);
+  if ((int64_t)d->max_blocks_per_seq * pa::kBlockSize + d->num_tokens > (int64_t)0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "prefix bound plus num_tokens exceeds 2^31 - 1 keys");
   if (d->num_kv_heads > 65535 || d->num_seqs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "num_kv_heads and num_seqs must be <= 65535 (grid limits)");
   return ok();

@@ -240,28 +240,56 @@ __device__ __forceinline__ int plan_tiles(int c, int L, int xb, int kpos) {
   return (c + min(L, (xb + 1) * kpos) + kTile - 1) / kTile;
 }
 
-// Exclusive prefix sum over the 512 threads of a work-group (v = 0 past the data);
-// *total receives the sum.  s_tmp: 8 words of LDS.
-__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+// Chunks of a row block of t tiles for chunk length C (C up to 2^31 - 1: no overflow).
+__device__ __forceinline__ int chunks_of(int t, int C) { return t / C + (t % C != 0); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes, then the last lane of row 0 added to row 1, of row 2 to
+// row 3, and of row 1 to rows 2 and 3 (a lane with no source in a step adds 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sums over the 512 threads of a work-group of N values per thread
+// (0 past the data), one pair of barriers for all N; tot[i] receives the sum of the i-th.
+// s_tmp: 8 N words of LDS.
+template <int N>
+__device__ void block_exclusive_scans(const int (&v)[N], int (&ex)[N], int (&tot)[N], int* s_tmp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
+  int incl[N];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) s_tmp[w] = incl;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int x = s_tmp[i];
-    off += i < w ? x : 0;
-    tot += x;
+  for (int i = 0; i < N; ++i) {
+    incl[i] = wave_inclusive_scan(v[i]);
+    if (lane == 63) s_tmp[8 * i + w] = incl[i];
   }
   __syncthreads();
-  *total = tot;
-  return off + incl - v;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int off = 0, t = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int x = s_tmp[8 * i + k];
+      off += k < w ? x : 0;
+      t += x;
+    }
+    ex[i] = off + incl[i] - v[i];
+    tot[i] = t;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int in[1] = {v};
+  int ex[1], tot[1];
+  block_exclusive_scans<1>(in, ex, tot, s_tmp);
+  *total = tot[0];
+  return ex[0];
 }
 
 // One work-group of 512 threads; S <= kOrderMaxSeqs sequences; kpos query positions per
@@ -270,7 +298,8 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   __shared__ int s_c[kOrderMaxSeqs], s_r0[kOrderMaxSeqs], s_L[kOrderMaxSeqs];
   __shared__ int s_npb[kOrderMaxSeqs], s_order[kOrderMaxSeqs], s_rbpre[kOrderMaxSeqs + 1];
   __shared__ int s_bucket[kSizeKeys];  // items per size key, then the key's next position
-  __shared__ int s_tmp[8];
+  __shared__ int s_tmp[24];
+  __shared__ int s_bad;
   __shared__ unsigned long long s_wsum;
   const int tid = threadIdx.x;
   const int cap = a.MB * kBlockSize;
@@ -287,7 +316,10 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     s_npb[tid] = (min(r1 - r0, a.max_query_len) + kpos - 1) / kpos;
   }
   for (int k = tid; k < kSizeKeys; k += blockDim.x) s_bucket[k] = 0;
-  if (tid == 0) s_wsum = 0;
+  if (tid == 0) {
+    s_wsum = 0;
+    s_bad = 0;
+  }
   __syncthreads();
   // Sequences most keys first (prefix plus new tokens; ties by index).
   if (tid < S) {
@@ -323,9 +355,12 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   __syncthreads();
   const unsigned long long W = s_wsum * (unsigned long long)H;
   const unsigned long long per = 5ull * (unsigned long long)max(a.ncu, 1);  // C >= W / 2.5N
-  long long C = a.chunk > 0 ? a.chunk
-                            : max((long long)kPrefillAutoMinChunk,
-                                  (long long)((2 * W + per - 1) / per));
+  // Tiles per row block stay below 2^25 (2^30 keys at most), so the per-row-block
+  // arithmetic below is 32-bit (64-bit division is a long software sequence).
+  int C = a.chunk > 0 ? a.chunk
+                      : (int)min(max((unsigned long long)kPrefillAutoMinChunk,
+                                     (2 * W + per - 1) / per),
+                                 (unsigned long long)0x7fffffff);
   // Pass 1 (twice at most): items per size key and the totals.  A plan beyond the sizes
   // the host provided for (not expected) falls back to whole row blocks, which fit.
   int nitems = 0, nslots = 0, ncut = 0;
@@ -334,17 +369,22 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
     for (int p = tid; p < nrb; p += blockDim.x) {
       int b, xb;
       row_block(p, b, xb);
-      const long long t = plan_tiles(s_c[b], s_L[b], xb, kpos);
-      const int nch = (int)((t + C - 1) / C);
-      const int key = (int)min((t + nch - 1) / nch, (long long)kSizeKeys - 1);
+      const int t = plan_tiles(s_c[b], s_L[b], xb, kpos);
+      const int nch = chunks_of(t, C);
+      const int key = min((t + nch - 1) / nch, kSizeKeys - 1);
       atomicAdd(&s_bucket[key], H * nch);
       li += H * nch;
       ls += nch > 1 ? H * nch : 0;
       lc += nch > 1 ? H : 0;
     }
-    (void)block_exclusive_scan(li, s_tmp, &nitems);
-    (void)block_exclusive_scan(ls, s_tmp, &nslots);
-    (void)block_exclusive_scan(lc, s_tmp, &ncut);
+    {
+      const int in[3] = {li, ls, lc};
+      int ex[3], tot[3];
+      block_exclusive_scans<3>(in, ex, tot, s_tmp);
+      nitems = tot[0];
+      nslots = tot[1];
+      ncut = tot[2];
+    }
     if (nitems <= a.item_bound && nslots <= a.slot_bound && ncut <= a.cut_bound) break;
     C = 0x7fffffff;
     for (int k = tid; k < kSizeKeys; k += blockDim.x) s_bucket[k] = 0;
@@ -383,39 +423,51 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   for (int p0 = 0; p0 < nrb; p0 += blockDim.x) {
     const int p = p0 + tid;
     int b = 0, xb = 0, nch = 0, key = -1;
-    long long t = 0;
+    int t = 0;
     if (p < nrb) {
       row_block(p, b, xb);
       t = plan_tiles(s_c[b], s_L[b], xb, kpos);
-      nch = (int)((t + C - 1) / C);
-      key = (int)min((t + nch - 1) / nch, (long long)kSizeKeys - 1);
+      nch = chunks_of(t, C);
+      key = min((t + nch - 1) / nch, kSizeKeys - 1);
     }
-    int nsl = 0, ncu = 0;
-    const int sl = block_exclusive_scan(nch > 1 ? H * nch : 0, s_tmp, &nsl);  // has barriers
-    const int cu = block_exclusive_scan(nch > 1 ? H : 0, s_tmp, &ncu);
+    const int in[2] = {nch > 1 ? H * nch : 0, nch > 1 ? H : 0};
+    int ex[2], tot[2];
+    block_exclusive_scans<2>(in, ex, tot, s_tmp);  // has barriers
+    const int sl = ex[0], cu = ex[1], nsl = tot[0], ncu = tot[1];
     if (p < nrb) {
       const int pos = atomicAdd(&s_bucket[key], H * nch);
+      // Inside the list, slots and counters by construction (the totals were checked
+      // against the bounds); tested here as well, so that no store can leave them (a
+      // plan that failed it would list nothing, below).
+      const bool fits = pos + H * nch <= nitems &&
+                        (nch == 1 || (slot_base + sl + H * nch <= nslots &&
+                                      cut_base + cu + H <= ncut));
+      if (!fits) s_bad = 1;
+      if (fits)
       for (int g = 0; g < H; ++g)
         for (int k = 0; k < nch; ++k) {
           // Words kItB .. kItNt as three 16-byte stores.
           typedef int i32x4 __attribute__((ext_vector_type(4)));
           i32x4* e = reinterpret_cast<i32x4*>(items + (size_t)(pos + g * nch + k) * kItemWords);
-          const int tb = (int)(k * t / nch);
+          // Balanced cut: the first t mod nch chunks get one tile more.
+          const int q = t / nch, r = t - q * nch;
+          const int tb = k * q + min(k, r);
           static_assert(kItB == 0 && kItNch == 4 && kItTb == 10 && kItNt == 11, "entry layout");
           e[0] = i32x4{b, g, xb, k};
           e[1] = i32x4{nch, nch > 1 ? slot_base + sl + g * nch + k : 0, nch > 1 ? cut_base + cu + g : 0,
                        s_c[b]};
-          e[2] = i32x4{s_r0[b], s_L[b], tb, (int)((k + 1) * t / nch) - tb};
+          e[2] = i32x4{s_r0[b], s_L[b], tb, q + (k < r ? 1 : 0)};
         }
     }
     slot_base += nsl;
     cut_base += ncu;
   }
+  __syncthreads();
   if (tid == 0) {
     a.plan[0] = (int)C;
-    a.plan[1] = nslots;
-    a.plan[2] = nitems;
-    a.plan[3] = ncut;
+    a.plan[1] = s_bad ? 0 : nslots;
+    a.plan[2] = s_bad ? 0 : nitems;
+    a.plan[3] = s_bad ? 0 : ncut;
   }
 }
 

@@ -427,6 +427,7 @@ PF_FAKE = [ctypes.c_void_p(0x20000 + 0x1000 * i) for i in range(9)]
     (dict(block_size=32), -6),
     (dict(num_q_heads=96, num_kv_heads=4), -6),   # G = 24
     (dict(num_kv_heads=70000, num_q_heads=70000), -6),
+    (dict(max_blocks_per_seq=(1 << 26) - 1, num_tokens=(1 << 30) + 100), -6),  # > 2^31 keys
 ])
 def test_prefill_validation(kw, status):
     st = B.lib().pa_prefill(ctypes.byref(pdims(**kw)), *PF_FAKE, 0.1, None)
