@@ -87,6 +87,11 @@ struct Shape {
 static_assert(Shape<128>::ROWS == prefill_rows(128) && Shape<256>::ROWS == prefill_rows(256),
               "work-group rows as the host sizes the partial states");
 
+// A row of zeros (head_dim 256 at most) for tile rows outside the keys.  Never written;
+// not const, so that it lives in global memory like the caches and a choice between it
+// and a cache row stays a global (not a flat) load.
+__device__ __attribute__((aligned(16))) uint16_t kZeroRow[256];
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool BF>
@@ -114,6 +119,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
+// Larger of two floats, NaN if either is (IEEE maximum: one v_maximum3_f32 for up to three
+// operands, where the NaN-ignoring fmaxf first quiets each operand with a v_max of itself).
+__device__ __forceinline__ float fmax_p(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
 // max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of one MFMA column),
 // with the two gfx950 half-swaps (upper 32 lanes with lower 32, odd 16-lane rows with
 // even ones).  The swapped pair is passed through an empty asm: without it the compiler
@@ -123,11 +132,11 @@ __device__ __forceinline__ float max_over_groups(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   uint32_t a0 = a[0], a1 = a[1];
   asm("" : "+v"(a0), "+v"(a1));
-  u = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1)));
+  u = __builtin_bit_cast(uint32_t, fmax_p(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1)));
   const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   uint32_t b0 = b[0], b1 = b[1];
   asm("" : "+v"(b0), "+v"(b1));
-  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+  return fmax_p(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
 // sum over lanes l, l ^ 16, l ^ 32, l ^ 48, with the same half-swaps; the result is
@@ -598,62 +607,81 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   f32x4 Lacc[kSumMfma ? CG : 1];
   const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0
   float m_ref[CG];
+  float negm[CG];  // -m_ref, or 0 while m_ref is -inf
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     m_ref[cg] = kNegInf;
+    negm[cg] = 0.f;
     lsum[cg] = 0.f;
     if constexpr (kSumMfma) Lacc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- tile loads: thread tid moves XC chunks (lc, lc + 8, ...) of K and of V of tile row tid/8 ----
-  // Loads are unconditional (a row outside the keys reads a valid dummy row and is
-  // zeroed when written to LDS).  Block ids are read one tile ahead of their use.
-  const int lrow = tid >> 3, lc = tid & 7;  // chunks lc + 8 i of row lrow
+  // The 8 rows of a wave (rows 8 w .. 8 w + 7 of a tile) lie in one 16-token cache block,
+  // so the block id is one value per wave, read with one uniform load a tile ahead of its
+  // use.  A wave whose 8 rows are all prefix keys, or all new tokens, loads them from a
+  // wave-uniform base plus a per-lane offset that is the same for every tile (no vector
+  // address arithmetic); the waves that hold the end of the prefix or of the keys address
+  // each row on its own, and a row outside the keys, or a prefix row whose block id is out
+  // of range, reads a row of zeros.  Every phase issues its loads, also past the last tile.
+  const int lrow = tid >> 3, lc = tid & 7;  // chunks lc + 8 i of row lrow = 8 w + jrow
+  const int jrow = lane >> 3;
   const size_t hstride = (size_t)kBlockSize * D;  // elements per (block, head)
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (size_t)g * hstride;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (size_t)g * hstride;
-  const uint16_t* knew = static_cast<const uint16_t*>(a.k_new);
-  const uint16_t* vnew = static_cast<const uint16_t*>(a.v_new);
-  const size_t bstride = (size_t)a.Hkv * hstride;
-  const int32_t* btrow = a.bt + (size_t)b * a.MB;
+  const char* const kc = static_cast<const char*>(a.k_cache) + (size_t)g * hstride * 2;
+  const char* const vc = static_cast<const char*>(a.v_cache) + (size_t)g * hstride * 2;
+  const char* const knew = static_cast<const char*>(a.k_new) + (size_t)g * D * 2;
+  const char* const vnew = static_cast<const char*>(a.v_new) + (size_t)g * D * 2;
+  const size_t bstride = (size_t)a.Hkv * hstride * 2;  // bytes per cache block
+  const size_t nstride = (size_t)a.Hkv * D * 2;        // bytes per new token
   const int cmax = c > 0 ? c - 1 : 0;
-  // Tile t of the loop is tile tb + t of the row block.
-  auto fetch_block = [&](int t) {  // block id of this thread's row of tile t (any if not prefix)
-    return btrow[min((tb + t) * kTile + lrow, cmax) / kBlockSize];
+  // Byte offsets of this lane's first chunk: in the wave's rows of a cache block, and in
+  // its rows of the new tokens.
+  const uint32_t off_pre = (uint32_t)((((8 * w) % kBlockSize + jrow) * D + 8 * lc) * 2);
+  const uint32_t off_new = (uint32_t)(jrow * nstride + 16 * lc);
+  // First key of this wave's rows in tile t (tile t of the loop is tile tb + t of the row block).
+  auto wave_key = [&](int t) { return (tb + t) * kTile + 8 * w; };
+  const __amdgpu_buffer_rsrc_t bt_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.bt + (size_t)b * a.MB), (short)0, a.MB * 4, 0x00020000);
+  auto fetch_block = [&](int t) {  // block id of this wave's rows of tile t (any if not prefix)
+    const int i = min(wave_key(t), cmax) / kBlockSize;
+    return __builtin_amdgcn_readfirstlane(
+        (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rs, 0, i * 4, 0));
   };
-  // Row lrow of tile t: source element offset in the cache (pre) or the new tokens.
-  auto row_source = [&](int t, int blk, bool& pre, bool& ok) -> size_t {
-    const int key = (tb + t) * kTile + lrow;
-    pre = key < c && (unsigned)blk < (unsigned)a.NB;
-    const bool fresh = key >= c && key < nkeys;
-    ok = pre || fresh;
-    return pre ? (size_t)blk * bstride + (size_t)(key % kBlockSize) * D
-               : (fresh ? ((size_t)(r0 + key - c) * a.Hkv + g) * D : (size_t)r0 * a.Hkv * D);
+  // Wave-uniform rows: a buffer resource at the wave's base (scalar arithmetic only).
+  auto load_uniform = [&](u32x4 (&r)[XC], const char* base, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < XC; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 128 * i, 0, 0));
+  };
+  auto load_rows = [&](u32x4 (&r)[XC], const char* cache, const char* fresh, int t, int blk) {
+    const int kb = wave_key(t);
+    if (kb + 8 <= c && (unsigned)blk < (unsigned)a.NB) {  // all prefix rows
+      load_uniform(r, cache + (size_t)blk * bstride, off_pre);
+    } else if (kb >= c && kb + 8 <= nkeys) {  // all new tokens
+      load_uniform(r, fresh + (size_t)(r0 + kb - c) * nstride, off_new);
+    } else {
+      const int key = kb + jrow;
+      const bool pre = key < c && (unsigned)blk < (unsigned)a.NB;
+      const bool nw = key >= c && key < nkeys;
+      const char* src = pre ? cache + (size_t)blk * bstride + off_pre
+                            : (nw ? fresh + (size_t)(r0 + key - c) * nstride + 16 * lc
+                                  : reinterpret_cast<const char*>(kZeroRow) + 16 * lc);
+#pragma unroll
+      for (int i = 0; i < XC; ++i) r[i] = *reinterpret_cast<const u32x4*>(src + 128 * i);
+    }
   };
   u32x4 kr[XC], vr[XC];
-  bool ok_k = false, ok_v = false;
-  auto load_k = [&](int t, int blk) {
-    bool pre;
-    const size_t off = row_source(t, blk, pre, ok_k);
-    const uint16_t* src = (pre ? kc : knew) + off;
+  auto load_k = [&](int t, int blk) { load_rows(kr, kc, knew, t, blk); };
+  auto load_v = [&](int t, int blk) { load_rows(vr, vc, vnew, t, blk); };
+  auto store_rows = [&](u32x4* dst, const u32x4 (&r)[XC]) {
 #pragma unroll
-    for (int i = 0; i < XC; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
-  };
-  auto load_v = [&](int t, int blk) {
-    bool pre;
-    const size_t off = row_source(t, blk, pre, ok_v);
-    const uint16_t* src = (pre ? vc : vnew) + off;
-#pragma unroll
-    for (int i = 0; i < XC; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 8 * (lc + 8 * i));
-  };
-  auto store_rows = [&](u32x4* dst, const u32x4 (&r)[XC], bool ok) {
-    const u32x4 z = {0u, 0u, 0u, 0u};  // zero: tail rows, prefix rows with a bad block id
-#pragma unroll
-    for (int i = 0; i < XC; ++i) dst[lrow * ROW + lc + 8 * i] = ok ? r[i] : z;
+    for (int i = 0; i < XC; ++i) dst[lrow * ROW + lc + 8 * i] = r[i];
   };
   // V rows as the PV products take them: bf16 converted to fp16 in the one-part form (a
   // value beyond fp16's range becomes an infinity; see the end of the kernel).
-  auto store_v = [&](u32x4* dst, const u32x4 (&r)[XC], bool ok) {
+  auto store_v = [&](u32x4* dst, const u32x4 (&r)[XC]) {
     if constexpr (kCvtV) {
       u32x4 c[XC];
 #pragma unroll
@@ -664,9 +692,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
           c[i][e] = pack2<false>(__builtin_bit_cast(float, wv << 16),
                                  __builtin_bit_cast(float, wv & 0xffff0000u));
         }
-      store_rows(dst, c, ok);
+      store_rows(dst, c);
     } else {
-      store_rows(dst, r, ok);
+      store_rows(dst, r);
     }
   };
 
@@ -674,8 +702,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     const int blk0 = fetch_block(0);
     load_k(0, blk0);
     load_v(0, blk0);
-    store_rows(s_k[0], kr, ok_k);
-    store_v(s_v[0], vr, ok_v);
+    store_rows(s_k[0], kr);
+    store_v(s_v[0], vr);
   }
   int blk_k = fetch_block(1), blk_v = blk_k;
   load_k(1, blk_k);
@@ -808,7 +836,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
             S[rb][cg][i] = vis ? S[rb][cg][i] * sl : kNegInf;
           }
         }
-        mx = fmaxf(mx, fmaxf(fmaxf(S[rb][cg][0], S[rb][cg][1]), fmaxf(S[rb][cg][2], S[rb][cg][3])));
+        mx = fmax_p(fmax_p(mx, fmax_p(S[rb][cg][0], S[rb][cg][1])), fmax_p(S[rb][cg][2], S[rb][cg][3]));
       }
       mx = max_over_groups(mx);
       bm[cg] = diag ? mx : mx * sl;
@@ -820,6 +848,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         const float m_new = fmaxf(m_ref[cg], bm[cg]);
         const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
         m_ref[cg] = m_new;
+        negm[cg] = m_new == kNegInf ? 0.f : -m_new;
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kg + i);
@@ -834,15 +863,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
         }
       }
     }
-    // m_ref is finite here except in a chunk of the planned schedule: key 0 is visible to
-    // every row and lies in tile 0.
+    // m_ref is finite here except in a chunk of the planned schedule (key 0 is visible to
+    // every row and lies in tile 0): a chunk that starts inside the causal part can hold no
+    // visible key for some rows yet, and negm = 0 gives them p = 0 until one appears.
     const float fs = diag ? 1.f : sl;  // diagonal tiles hold scaled logits already
     const f16x2 ones2 = {(_Float16)1.f, (_Float16)1.f};  // one-part row sums: p0 + p1 + sum
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      // A chunk of the planned schedule that starts inside the causal part can hold no
-      // visible key for some rows yet: p = 0 for them until one appears.
-      const float nm = (kSched == 2 && m_ref[cg] == kNegInf) ? 0.f : -m_ref[cg];
+      const float nm = negm[cg];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float p[8];
@@ -878,15 +906,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // buffers of each hold.
   // Tile traffic of a phase: write tile u + 1 to LDS, request tile u + 2.  Both happen
   // in every phase, also past the last tile (the buffer written is not read again, the
-  // rows requested are valid dummy rows): with no branch around them the compiler's wait
-  // counts stay exact, and no wait drains the loads still in flight.
+  // rows requested are zero rows): with no branch around them the compiler's wait counts
+  // stay exact, and no wait drains the loads still in flight.
   auto io_k = [&](int u) {
-    store_rows(s_k[(u + 1) & 1], kr, ok_k);
+    store_rows(s_k[(u + 1) & 1], kr);
     load_k(u + 2, blk_k);
     blk_k = fetch_block(u + 3);
   };
   auto io_v = [&](int u) {
-    store_v(s_v[(u + 1) & 1], vr, ok_v);
+    store_v(s_v[(u + 1) & 1], vr);
     load_v(u + 2, blk_v);
     blk_v = fetch_block(u + 3);
   };
