@@ -681,21 +681,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   };
   // V rows as the PV products take them: bf16 converted to fp16 in the one-part form (a
   // value beyond fp16's range becomes an infinity; see the end of the kernel).
-  auto store_v = [&](u32x4* dst, const u32x4 (&r)[XC]) {
+  auto cvt_v = [&](u32x4 (&r)[XC]) {
     if constexpr (kCvtV) {
-      u32x4 c[XC];
 #pragma unroll
       for (int i = 0; i < XC; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t wv = r[i][e];
-          c[i][e] = pack2<false>(__builtin_bit_cast(float, wv << 16),
+          r[i][e] = pack2<false>(__builtin_bit_cast(float, wv << 16),
                                  __builtin_bit_cast(float, wv & 0xffff0000u));
         }
-      store_rows(dst, c);
-    } else {
-      store_rows(dst, r);
     }
+  };
+  auto store_v = [&](u32x4* dst, u32x4 (&r)[XC]) {
+    cvt_v(r);
+    store_rows(dst, r);
   };
 
   {
@@ -913,8 +913,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     load_k(u + 2, blk_k);
     blk_k = fetch_block(u + 3);
   };
-  auto io_v = [&](int u) {
-    store_v(s_v[(u + 1) & 1], vr);
+  // cvt: convert bf16 V here (group 0, in its matrix phase); group 1 converts it in its
+  // matrix phase, one phase before this store, so that its softmax phase does not.
+  auto io_v = [&](int u, bool cvt) {
+    if (cvt)
+      store_v(s_v[(u + 1) & 1], vr);
+    else
+      store_rows(s_v[(u + 1) & 1], vr);
     load_v(u + 2, blk_v);
     blk_v = fetch_block(u + 3);
   };
@@ -931,16 +936,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     _Pragma("unroll") for (int cg = 0; cg < CG; ++cg)                                 \
       _Pragma("unroll") for (int j = 0; j < JD; ++j) asm("" : "+v"(O[cg][j]));         \
     if (GRP == 0) {                                                                    \
-      if (t_ >= 1) io_v(t_ - 1); /* phase 0 has no traffic */                          \
+      if (t_ >= 1) io_v(t_ - 1, true); /* phase 0 has no traffic */                    \
     } else {                                                                           \
       io_k(t_);                                                                        \
+      cvt_v(vr); /* V of tile t + 1, stored in the next phase */                       \
     }                                                                                  \
     __syncthreads();                                                                   \
     if (t_ < ntiles) softmax(t_);                                                      \
     if (GRP == 0)                                                                      \
       io_k(t_);                                                                        \
     else                                                                               \
-      io_v(t_);                                                                        \
+      io_v(t_, false);                                                                 \
     __syncthreads();                                                                   \
   } while (0)
   if (grp == 0) {
