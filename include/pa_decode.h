@@ -52,6 +52,14 @@
  * read on the device.  Block ids outside [0, NB) are read as block 0 and a
  * context length above MB*16 is clamped to MB*16: such inputs give
  * unspecified results but never an access outside the caller's buffers.
+ *
+ * Scheduling (performance only; results never depend on it).  With 2..512
+ * sequences the V2 kernel dispatches only the partitions that exist,
+ * contiguously, and V1 on the four-wave matrix-core shape (at least 256
+ * (sequence, KV head) pairs, tables over 1024 tokens) takes sequences longest
+ * context first.  Each work-group derives its item from all S context lengths
+ * on the device.  Above 512 sequences both kernels take their items in grid
+ * order: V2 launches every partition slot and the empty ones return at once.
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H
