@@ -410,7 +410,9 @@ pa_status_t pa_copy_blocks_profiled(void* k_cache, void* v_cache, int64_t block_
  * (others: PA_ERR_UNSUPPORTED).  query_start must be non-decreasing from 0 with
  * query_start[S] <= T (rows past T are not read or written); a context length is
  * clamped to MB*16.  max_query_len bounds every L_b and sizes the grid (<= 0: T);
- * a longer chunk is computed only for its first max_query_len tokens.
+ * a longer chunk is computed only for its first max_query_len tokens.  A prefix
+ * block id outside [0, NB) reads its 16 tokens as zero keys and zero values (each
+ * still takes a softmax weight, with logit 0): no access leaves the caller's buffers.
  */
 typedef struct pa_prefill_dims {
   int32_t num_seqs;            /* S */

@@ -182,6 +182,35 @@ def test_determinism_placement_and_poison():
     assert torch.equal(run(w3, upload(w3)), a), "cache contents outside the prefix were read"
 
 
+def test_out_of_range_block_ids_read_as_zero_rows():
+    """A prefix block id outside [0, NB) (-1, NB, NB + 1000, 2^31 - 1) reads its tokens as
+    zero keys and values, as the header states: the output equals the oracle's on a pool
+    with an all-zero block at those table entries.  The broken blocks sit in whole-wave
+    prefix rows, in a wave whose rows run from the prefix into the new tokens, and in
+    the first block of a prefix."""
+    w = wl.make_prefill_workload("badid", 91, context_lens=[200, 77, 40], query_lens=[33, 20, 64],
+                                 num_q_heads=16, num_kv_heads=2, head_dim=128, dtype="bf16")
+    NB = w.k_cache.shape[0]
+    bad = [(0, 2, -1), (0, 5, NB), (1, 4, NB + 1000), (2, 0, 2**31 - 1)]
+    bt_gpu = w.block_tables.copy()
+    bt_ref = w.block_tables.copy()
+    for b, j, bid in bad:
+        assert j < -(-int(w.context_lens[b]) // 16), "the broken block must lie in the prefix"
+        bt_gpu[b, j] = bid
+        bt_ref[b, j] = NB  # the appended zero block
+    kz = np.concatenate([w.k_cache, np.zeros_like(w.k_cache[:1])])
+    vz = np.concatenate([w.v_cache, np.zeros_like(w.v_cache[:1])])
+    w_gpu = wl.PrefillWorkload(w.name, w.dtype, w.q, w.k_new, w.v_new, w.k_cache, w.v_cache,
+                               bt_gpu, w.context_lens, w.query_start, w.scale, w.pad_block,
+                               w.seed)
+    w_ref = wl.PrefillWorkload(w.name, w.dtype, w.q, w.k_new, w.v_new, kz, vz, bt_ref,
+                               w.context_lens, w.query_start, w.scale, w.pad_block, w.seed)
+    say("prefill out-of-range block ids")
+    got = to_f64(run(w_gpu, upload(w_gpu)))
+    assert np.isfinite(got).all()
+    check_rows(got, reference(w_ref), "prefill out-of-range block ids")
+
+
 def test_max_query_len_bounds_the_rows_written():
     w = wl.make_prefill_workload("mq", 78, context_lens=[20, 5], query_lens=[300, 40],
                                  num_q_heads=8, num_kv_heads=1, head_dim=128, dtype="f16")
