@@ -642,10 +642,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   auto wave_key = [&](int t) { return (tb + t) * kTile + 8 * w; };
   const __amdgpu_buffer_rsrc_t bt_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(a.bt + (size_t)b * a.MB), (short)0, a.MB * 4, 0x00020000);
-  auto fetch_block = [&](int t) {  // block id of this wave's rows of tile t (any if not prefix)
+  // Block id of this wave's rows of tile t (any if not prefix), as loaded (every lane
+  // holds it).  take_block moves it to a scalar register where it is used, a phase after
+  // the load, ahead of the next id's load into the same register; as the builtin, the
+  // compiler hoisted that move to the top of the phase, where waiting for the id also
+  // waited for the tile loads issued after it.
+  auto fetch_block = [&](int t) {
     const int i = min(wave_key(t), cmax) / kBlockSize;
-    return __builtin_amdgcn_readfirstlane(
-        (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rs, 0, i * 4, 0));
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rs, 0, i * 4, 0);
+  };
+  auto take_block = [](int v) {
+    int r;
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));
+    return r;
   };
   // Wave-uniform rows: a buffer resource at the wave's base (scalar arithmetic only).
   auto load_uniform = [&](u32x4 (&r)[XC], const char* base, uint32_t off) {
@@ -662,12 +671,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     } else if (kb >= c && kb + 8 <= nkeys) {  // all new tokens
       load_uniform(r, fresh + (size_t)(r0 + kb - c) * nstride, off_new);
     } else {
+      // Per row: one of three wave-uniform bases plus a per-lane offset (the new-token
+      // base is that of key kb, before the prefix end for some rows, never used for them).
       const int key = kb + jrow;
       const bool pre = key < c && (unsigned)blk < (unsigned)a.NB;
       const bool nw = key >= c && key < nkeys;
-      const char* src = pre ? cache + (size_t)blk * bstride + off_pre
-                            : (nw ? fresh + (size_t)(r0 + key - c) * nstride + 16 * lc
-                                  : reinterpret_cast<const char*>(kZeroRow) + 16 * lc);
+      const char* pbase = cache + (size_t)blk * bstride;
+      const char* nbase = fresh + (ptrdiff_t)(r0 + kb - c) * (ptrdiff_t)nstride;
+      const char* zbase = reinterpret_cast<const char*>(kZeroRow);
+      const char* src = pre ? pbase + off_pre : (nw ? nbase + off_new : zbase + 16 * lc);
 #pragma unroll
       for (int i = 0; i < XC; ++i) r[i] = *reinterpret_cast<const u32x4*>(src + 128 * i);
     }
@@ -699,17 +711,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   };
 
   {
-    const int blk0 = fetch_block(0);
+    const int blk0 = take_block(fetch_block(0));
     load_k(0, blk0);
     load_v(0, blk0);
     store_rows(s_k[0], kr);
     store_v(s_v[0], vr);
   }
-  int blk_k = fetch_block(1), blk_v = blk_k;
-  load_k(1, blk_k);
-  load_v(1, blk_v);
-  blk_k = fetch_block(2);
-  blk_v = blk_k;
+  {
+    const int blk1 = take_block(fetch_block(1));
+    load_k(1, blk1);
+    load_v(1, blk1);
+  }
+  int blk_k = fetch_block(2), blk_v = fetch_block(2);
   __syncthreads();
 
   f32x4 S[4][CG];  // [row block][cg]: S^T of the tile, keys 16rb + 4kg + i, query row r16
@@ -908,10 +921,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // in every phase, also past the last tile (the buffer written is not read again, the
   // rows requested are zero rows): with no branch around them the compiler's wait counts
   // stay exact, and no wait drains the loads still in flight.
+  // The next block id is requested before the tile loads, so that the wait for it, a
+  // phase later, does not include them.
   auto io_k = [&](int u) {
     store_rows(s_k[(u + 1) & 1], kr);
-    load_k(u + 2, blk_k);
+    const int blk = take_block(blk_k);
     blk_k = fetch_block(u + 3);
+    load_k(u + 2, blk);
   };
   // cvt: convert bf16 V here (group 0, in its matrix phase); group 1 converts it in its
   // matrix phase, one phase before this store, so that its softmax phase does not.
@@ -920,8 +936,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
       store_v(s_v[(u + 1) & 1], vr);
     else
       store_rows(s_v[(u + 1) & 1], vr);
-    load_v(u + 2, blk_v);
+    const int blk = take_block(blk_v);
     blk_v = fetch_block(u + 3);
+    load_v(u + 2, blk);
   };
   // One tile t of wave group GRP: the matrix phase 2t + GRP, then the softmax phase
   // 2t + GRP + 1.  Group 0 carries the V traffic in its matrix phase and the K traffic
