@@ -87,11 +87,6 @@ struct Shape {
 static_assert(Shape<128>::ROWS == prefill_rows(128) && Shape<256>::ROWS == prefill_rows(256),
               "work-group rows as the host sizes the partial states");
 
-// A row of zeros (head_dim 256 at most) for tile rows outside the keys.  Never written;
-// not const, so that it lives in global memory like the caches and a choice between it
-// and a cache row stays a global (not a flat) load.
-__device__ __attribute__((aligned(16))) uint16_t kZeroRow[256];
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool BF>
@@ -657,9 +652,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     return r;
   };
   // Wave-uniform rows: a buffer resource at the wave's base (scalar arithmetic only).
-  auto load_uniform = [&](u32x4 (&r)[XC], const char* base, uint32_t off) {
+  // (bytes: the resource's size; a load past it returns zeros and touches no memory)
+  auto load_uniform = [&](u32x4 (&r)[XC], const char* base, uint32_t off,
+                          int bytes = 0x7fffffff) {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < XC; ++i)
       r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 128 * i, 0, 0));
@@ -671,17 +668,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
     } else if (kb >= c && kb + 8 <= nkeys) {  // all new tokens
       load_uniform(r, fresh + (size_t)(r0 + kb - c) * nstride, off_new);
     } else {
-      // Per row: one of three wave-uniform bases plus a per-lane offset (the new-token
-      // base is that of key kb, before the prefix end for some rows, never used for them).
+      // Rows from both sources: the lanes of new-token rows load those (the new-token base
+      // is that of key kb, before the prefix end for the other lanes, which do not use
+      // it); the other lanes load from the cache block, through a resource of no bytes if
+      // the block id is out of range, and rows outside the keys read past the resource:
+      // zeros.  The two loads run under complementary lane masks into the same registers.
       const int key = kb + jrow;
-      const bool pre = key < c && (unsigned)blk < (unsigned)a.NB;
       const bool nw = key >= c && key < nkeys;
-      const char* pbase = cache + (size_t)blk * bstride;
-      const char* nbase = fresh + (ptrdiff_t)(r0 + kb - c) * (ptrdiff_t)nstride;
-      const char* zbase = reinterpret_cast<const char*>(kZeroRow);
-      const char* src = pre ? pbase + off_pre : (nw ? nbase + off_new : zbase + 16 * lc);
-#pragma unroll
-      for (int i = 0; i < XC; ++i) r[i] = *reinterpret_cast<const u32x4*>(src + 128 * i);
+      if (nw) {
+        load_uniform(r, fresh + (ptrdiff_t)(r0 + kb - c) * (ptrdiff_t)nstride, off_new);
+        // keeps the two branches' loads apart: merged into one load, its resource would be
+        // a per-lane choice, which the compiler lowers to a loop over lanes
+        asm volatile("" ::: "memory");
+      } else {
+        const bool blk_ok = (unsigned)blk < (unsigned)a.NB;
+        const bool pre = key < c && blk_ok;
+        load_uniform(r, blk_ok ? cache + (size_t)blk * bstride : cache, pre ? off_pre : 0x40000000u,
+                     blk_ok ? (int)bstride : 0);
+      }
     }
   };
   u32x4 kr[XC], vr[XC];
