@@ -616,9 +616,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // so the block id is one value per wave, read with one uniform load a tile ahead of its
   // use.  A wave whose 8 rows are all prefix keys, or all new tokens, loads them from a
   // wave-uniform base plus a per-lane offset that is the same for every tile (no vector
-  // address arithmetic); the waves that hold the end of the prefix or of the keys address
-  // each row on its own, and a row outside the keys, or a prefix row whose block id is out
-  // of range, reads a row of zeros.  Every phase issues its loads, also past the last tile.
+  // address arithmetic); the waves that hold the end of the prefix or of the keys load
+  // from both sources under complementary lane masks.  A row outside the keys, or a prefix
+  // row whose block id is out of range, reads zeros (past the end of its buffer resource).
+  // Every phase issues its loads, also past the last tile.
   const int lrow = tid >> 3, lc = tid & 7;  // chunks lc + 8 i of row lrow = 8 w + jrow
   const int jrow = lane >> 3;
   const size_t hstride = (size_t)kBlockSize * D;  // elements per (block, head)
@@ -923,8 +924,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   // buffers of each hold.
   // Tile traffic of a phase: write tile u + 1 to LDS, request tile u + 2.  Both happen
   // in every phase, also past the last tile (the buffer written is not read again, the
-  // rows requested are zero rows): with no branch around them the compiler's wait counts
-  // stay exact, and no wait drains the loads still in flight.
+  // rows requested read as zeros): with no branch around them the compiler's wait counts
+  // stay close, and no wait drains the loads still in flight.
   // The next block id is requested before the tile loads, so that the wait for it, a
   // phase later, does not include them.
   auto io_k = [&](int u) {
