@@ -485,8 +485,8 @@ int32_t pa_get_prefill_mode(void);
  * sequence and KV head, P = 256 / G query positions at head_dim 128, 128 / G at 256)
  * attends to its keys in 64-key tiles, t of them.  -1 (default): a plan kernel reads the
  * context and chunk lengths on the device, cuts every row block of more than C tiles
- * into ceil(t / C) chunks (C = max(16, ceil(2W / 5N)) for W tiles in the call and N
- * compute units), and lists the items (chunks and whole row blocks, per KV head) largest
+ * into ceil(t / C) chunks (C = max(16, ceil(5W / 4N)) for W tiles in the call and N
+ * compute units: only row blocks longer than 1.25 units' fair share are cut), and lists the items (chunks and whole row blocks, per KV head) largest
  * first; the prefill kernel takes them in that order, and the last chunk of a row block
  * to finish folds its chunks with the log-sum-exp rule (the same statistics as decode's
  * Phase 2, over key ranges instead of partitions).  k in 4 .. 2^20: chunks of at most k

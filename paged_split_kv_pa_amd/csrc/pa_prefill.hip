@@ -211,8 +211,9 @@ __device__ __forceinline__ int seq_of_key_rank(const PrefillArgs& a, int S, int 
 // blocks differ in length (a long prefix next to short ones, or a few row blocks over a
 // long prefix) ends on its longest row blocks alone.  The planned schedule cuts every
 // row block of more than C tiles into nch = ceil(t / C) chunks of consecutive tiles (C =
-// max(16, ceil(2W / 5N)) for W tiles in the launch over N compute units: about 2.5
-// chunks' worth of work per unit; 2N and 3N measured slower) and lists the items (a
+// max(16, ceil(5W / 4N)) for W tiles in the launch over N compute units: a chunk holds at
+// most 1.25 units' fair share, and only row blocks longer than that are cut, since every
+// extra chunk costs a partial write and its share of a fold) and lists the items (a
 // chunk, or a whole row block, of one KV head) largest first; work-group j takes entry j
 // of the list, so the dispatcher hands out the work longest-processing-time first.
 //
@@ -358,12 +359,12 @@ __global__ void __launch_bounds__(512) prefill_plan_kernel(const PrefillArgs a, 
   }
   __syncthreads();
   const unsigned long long W = s_wsum * (unsigned long long)H;
-  const unsigned long long per = 5ull * (unsigned long long)max(a.ncu, 1);  // C >= W / 2.5N
+  const unsigned long long per = 4ull * (unsigned long long)max(a.ncu, 1);  // C >= 1.25 W / N
   // Tiles per row block stay below 2^25 (2^30 keys at most), so the per-row-block
   // arithmetic below is 32-bit (64-bit division is a long software sequence).
   int C = a.chunk > 0 ? a.chunk
                       : (int)min(max((unsigned long long)kPrefillAutoMinChunk,
-                                     (2 * W + per - 1) / per),
+                                     (5 * W + per - 1) / per),
                                  (unsigned long long)0x7fffffff);
   // Pass 1 (twice at most): items per size key and the totals.  A plan beyond the sizes
   // the host provided for (not expected) falls back to whole row blocks, which fit.
@@ -1240,9 +1241,9 @@ size_t prefill_plan_bytes(int head_dim, int group, int num_seqs, PrefillArgs& a)
   // call): the grid schedule, without the plan kernel's latency.
   if (a.chunk < 0 && per_rb <= 1) return 0;
   const long long N = std::max(a.ncu, 1);
-  // Automatic chunks: W / C <= 2.5N, so items <= 2.5N + R, chunks of cut row blocks
-  // <= 5N, cut row blocks <= 2.5N (the bounds below keep 3N and 6N).  A plan beyond these
-  // is dropped on the device for the uncut one.
+  // Automatic chunks: W / C <= 0.8N, so items <= 0.8N + R, chunks of cut row blocks
+  // <= 1.6N, cut row blocks <= 0.8N (the bounds below keep 3N and 6N).  A plan beyond
+  // these is dropped on the device for the uncut one.
   long long slots = per_rb > 1 ? R * per_rb : 0, merges = per_rb > 1 ? R : 0;
   if (a.chunk < 0) {
     slots = std::min(slots, 6 * N);
