@@ -840,31 +840,37 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
   auto softmax = [&](int t) {
     const int kbase = (tb + t) * kTile;
     const bool diag = kbase + kTile - 1 > c + p0;  // some key of the tile may lie after some row
-    float bm[CG];
+    // The row max only decides whether a row grows past its reference by more than the
+    // slack, and it does exactly when the max over some lane's 16 keys does: so each lane
+    // compares its own max, and the lanes' maxima are combined only on the (rare) rescale.
+    float pm[CG];  // this lane's max over its keys 16 rb + 4 kg + i of the tile
     bool grow = false;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      float mx = kNegInf;
+      if (diag) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (diag) {
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kbase + 16 * rb + 4 * kg + i;
             const bool vis = key <= c + qpos_col[cg] && key < nkeys;
             S[rb][cg][i] = vis ? S[rb][cg][i] * sl : kNegInf;
           }
-        }
-        mx = fmax_p(fmax_p(mx, fmax_p(S[rb][cg][0], S[rb][cg][1])), fmax_p(S[rb][cg][2], S[rb][cg][3]));
       }
-      mx = max_over_groups(mx);
-      bm[cg] = diag ? mx : mx * sl;
-      grow = grow || bm[cg] > m_ref[cg] + kRescaleSlack;
+      // a chain of three-operand maxima (v_maximum3_f32): 8 instructions for 16 values
+      float mx = fmax_p(fmax_p(S[0][cg][0], S[0][cg][1]), S[0][cg][2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2)
+        mx = fmax_p(fmax_p(mx, S[e / 4][cg][e % 4]), S[(e + 1) / 4][cg][(e + 1) % 4]);
+      mx = fmax_p(mx, S[3][cg][3]);
+      pm[cg] = mx;
+      grow = grow || (diag ? mx : mx * sl) > m_ref[cg] + kRescaleSlack;
     }
     if (__any(grow)) {  // rare
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        const float m_new = fmaxf(m_ref[cg], bm[cg]);
+        const float rmax = max_over_groups(pm[cg]);
+        const float m_new = fmaxf(m_ref[cg], diag ? rmax : rmax * sl);
         const float alpha = m_ref[cg] == kNegInf ? 0.f : exp2_fast(m_ref[cg] - m_new);
         m_ref[cg] = m_new;
         negm[cg] = m_new == kNegInf ? 0.f : -m_new;
