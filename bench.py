@@ -93,7 +93,45 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference "
                          "kernel for scaling hardware byte counters), then exit")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time dense square GEMMs (torch.matmul, bf16 and fp16, N(0,1) "
+                         "and all-zero operands): the matrix-core rate this card sustains, "
+                         "then exit")
+    ap.add_argument("--prefill-zero", choices=("none", "k", "v", "kv"), default="none",
+                    help="prefill: zero the cached and new keys and/or values (the same "
+                         "kernel and work on operands that draw less power)")
     return ap.parse_args()
+
+
+def gemm_reference(reps=20):
+    """Dense square GEMMs through torch.matmul (hipBLASLt) in bf16 and fp16, on N(0,1) and on
+    all-zero operands: the matrix-core rate a vendor GEMM sustains on this card, to read the
+    prefill rates against.  The zero operands draw less power, so the clock runs higher:
+    the gap between the two is the data-dependent part of the sustained rate."""
+    import torch
+    rec = {"metric": "dense GEMM TFLOP/s (torch.matmul)", "unit": "TFLOP/s", "n_gpus": 1,
+           "peak": MFMA_PEAK_TFLOPS_16BIT, "rates": []}
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for dt in (torch.bfloat16, torch.float16):
+        for n in (8192, 16384):
+            a = torch.randn(n, n, device="cuda", dtype=dt, generator=gen)
+            b = torch.randn(n, n, device="cuda", dtype=dt, generator=gen)
+            z = torch.zeros_like(a)
+            for name, (x, y) in (("randn", (a, b)), ("zeros", (z, z))):
+                for _ in range(3):
+                    torch.matmul(x, y)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    torch.matmul(x, y)
+                torch.cuda.synchronize()
+                tf = 2 * n ** 3 / ((time.perf_counter() - t0) / reps) / 1e12
+                rec["rates"].append({"dtype": str(dt).split(".")[-1], "n": n, "operands": name,
+                                     "tflops": round(tf, 1),
+                                     "of_peak": round(tf / MFMA_PEAK_TFLOPS_16BIT, 4)})
+                log(f"gemm {dt} n={n} {name}: {tf:.0f} TFLOP/s")
+            del a, b, z
+    print(json.dumps(rec), flush=True)
 
 
 def copy_calibration(mib, reps=5):
@@ -432,6 +470,10 @@ def bench_prefill(args):
                                                         "v_cache")}
     for n in ("block_tables", "context_lens", "query_start"):
         dev[n] = torch.from_numpy(np.ascontiguousarray(getattr(w, n), dtype=np.int32)).cuda()
+    zeroed = {"none": (), "k": ("k_new", "k_cache"), "v": ("v_new", "v_cache"),
+              "kv": ("k_new", "k_cache", "v_new", "v_cache")}[args.prefill_zero]
+    for n in zeroed:
+        dev[n].zero_()
     out = torch.empty_like(dev["q"])
     flops = prefill_flops(w)
     lib = B.lib()
@@ -490,7 +532,8 @@ def bench_prefill(args):
         "value": round(flops / (us / 1e6) / 1e12, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic" if not zeroed else "synthetic, zeroed " + "/".join(zeroed),
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_tokens": w.num_tokens,
                    "context_lens": [int(x) for x in w.context_lens],
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
@@ -501,7 +544,7 @@ def bench_prefill(args):
                      "kernel": "prefill_kernel", "kernel_mean_us": round(kmean, 3),
                      "kernel_samples": len(ker)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not zeroed:  # the oracle sees the workload's inputs
         import oracle
         from oracle.storage import upcast
         # parity of the first call on 16 sampled (row, head) outputs: the oracle computes
@@ -572,6 +615,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.gemm_reference:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        gemm_reference()
         return
     if args.sweep_paths:
         sweep_paths()
