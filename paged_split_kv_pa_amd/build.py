@@ -32,9 +32,12 @@ HIPCC_FLAGS = [
 # compiler copied them between the register files on every K/V tile.
 # The decode kernels take their latency-critical arguments as leading scalars (see
 # PA_ATTN_LEAD_PARAMS and PA_REDUCE_LEAD_PARAMS in pa_kernels.hip); the hardware preloads
-# those into registers.
+# those into registers.  Their accumulators stay in VGPRs too: at head_dim 256 (over 256
+# registers per lane) the AGPR form moved ~240 values between the register files per KV
+# block; at head_dim 128 the code is the same either way.
 SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"]}
+                "pa_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12",
+                                   "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():

@@ -875,9 +875,14 @@ __global__ void __launch_bounds__(NW * 64, D == 128 ? 2 : 1)
       u32x4* tile = reinterpret_cast<u32x4*>(s_un) + w * 16 * CPR;
 #pragma unroll
       for (int j = 0; j < NKK; ++j) {
-        const int cl = 64 * j + ql;
-        const int r = cl / CPR, c = cl % CPR;
-        tile[r * CPR + (c + r) % CPR] = kr[j];
+        // Unsigned arithmetic on a power-of-two row length: a few instructions per chunk.
+        // The one-wave two-deep shape has the registers to keep the slots (the same for
+        // every block) from the lane itself; the deeper or wider shapes, which would then
+        // spill, recompute them from the opaque lane index.
+        static_assert((CPR & (CPR - 1)) == 0, "K tile rows of a power-of-two chunk count");
+        const unsigned cl = 64u * j + (unsigned)(NW == 1 && NBUF == 2 ? lane : ql);
+        const unsigned r = cl / CPR, c = cl % CPR;
+        tile[r * CPR + ((c + r) & (CPR - 1))] = kr[j];
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
