@@ -848,14 +848,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const PrefillArgs 
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       if (diag) {
+        // key kbase + 16 rb + 4 kg + i is visible to this lane's row iff it is at most
+        // c + position and below nkeys, i.e. iff 16 rb + i <= lim (one compare with a
+        // constant per score)
+        const int lim = min(c + qpos_col[cg], nkeys - 1) - kbase - 4 * kg;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + 16 * rb + 4 * kg + i;
-            const bool vis = key <= c + qpos_col[cg] && key < nkeys;
-            S[rb][cg][i] = vis ? S[rb][cg][i] * sl : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i)
+            S[rb][cg][i] = 16 * rb + i <= lim ? S[rb][cg][i] * sl : kNegInf;
       }
       // a chain of three-operand maxima (v_maximum3_f32): 8 instructions for 16 values
       float mx = fmax_p(fmax_p(S[0][cg][0], S[0][cg][1]), S[0][cg][2]);
