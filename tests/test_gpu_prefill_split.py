@@ -7,10 +7,10 @@ page, V2 plan, applied to key ranges of one prefill row block).  Checked against
 float64 oracle at the decode tolerance: automatic chunks on the bench workloads and on a
 short chunk after a long prefix (the case the plan is for); fixed small chunks (4 to 16
 tiles) on ragged shapes at every group size and both head dims, including chunks that
-start inside the causal part; several hundred sequences; 513 sequences (beyond the plan:
-the grid schedule); results independent of the rest of the batch with a fixed chunk
-length (bitwise); the schedule off; a captured graph replayed; bf16 values beyond fp16
-in a cut row block (the two-part recompute)."""
+start inside the causal part; more than 512 row blocks; several hundred sequences; 513
+sequences (beyond the plan: the grid schedule); results independent of the rest of the
+batch with a fixed chunk length (bitwise); the schedule off; a captured graph replayed;
+bf16 values beyond fp16 in a cut row block (the two-part recompute)."""
 import contextlib
 import sys
 
@@ -151,6 +151,37 @@ def test_many_sequences(S):
     with split(8):
         got = run(w, upload(w))
     check_rows(to_f64(got), reference(w), f"{S} sequences")
+
+
+@pytest.mark.parametrize("chunk", (16, -1), ids=("c16", "auto"))
+def test_more_than_512_row_blocks(chunk):
+    """Two sequences whose chunks hold 519 + 40 row blocks of 16 positions (16 query heads
+    per KV head): the plan kernel's per-row-block loops, the tile total among them, run in
+    two rounds of its 512 threads.  Sampled (row, head) outputs against the oracle's causal
+    rows, one at a time."""
+    ctx, ql = [300, 5000], [8300, 640]
+    w = wl.make_prefill_workload("rb", 3900, context_lens=ctx, query_lens=ql, num_q_heads=16,
+                                 num_kv_heads=1, head_dim=128, dtype="bf16")
+    say(f"planned prefill {sum(-(-n // 16) for n in ql)} row blocks chunk {chunk}")
+    with split(chunk):
+        got = to_f64(run(w, upload(w)))
+    from oracle.storage import upcast
+    rng = np.random.default_rng(3901)
+    q, kn, vn = upcast(w.q, w.dtype), upcast(w.k_new, w.dtype), upcast(w.v_new, w.dtype)
+    s = float(np.float32(w.scale))
+    picks = [(0, 0), (0, 8299), (1, 0), (1, 639)] + [
+        (int(b), int(rng.integers(0, ql[int(b)]))) for b in rng.integers(0, 2, 40)]
+    ref, gs = [], []
+    for b, i in picks:
+        c, r0 = ctx[b], int(w.query_start[b])
+        kp = upcast(oracle.gather_sequence(w.k_cache, w.block_tables, b, c), w.dtype)[:, 0]
+        vp = upcast(oracle.gather_sequence(w.v_cache, w.block_tables, b, c), w.dtype)[:, 0]
+        h = int(rng.integers(0, 16))
+        ka = np.concatenate([kp, kn[r0:r0 + i + 1, 0]])
+        va = np.concatenate([vp, vn[r0:r0 + i + 1, 0]])
+        ref.append(oracle.prefill_rows(q[r0 + i:r0 + i + 1, h], ka, va, c + i, s)[0])
+        gs.append(got[r0 + i, h])
+    check_close(np.array(gs)[None], np.array(ref)[None], f"{len(picks)} sampled rows, chunk {chunk}")
 
 
 def test_off_matches_oracle_and_planned_agrees():
